@@ -1,0 +1,352 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, independent of the oracle's own formulas.
+
+Pages: [P1] "Performer — 랜덤 특징으로 어텐션을 다시 생각하기" (digest of
+*Rethinking Attention with Performers*); [P2] Su Jianlin, "From Performer to
+Linear Attention"; [P3] paperlayer.ai summary of arXiv:2009.14794v4.
+
+Every statistical test uses fixed seeds, so it is deterministic; the margins
+were set from the sampling error, not from the result.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.native as native
+import oracle.reference as ref
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# Features: deterministic identities and hand-worked values
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("impl", ["numpy", "c"])
+@pytest.mark.parametrize("m,d", [(1, 3), (7, 5), (32, 16), (40, 16)])
+def test_feature_identity_opposite_vectors(impl, m, d):
+    """phi(x).phi(-x) = exp(-|x|^2) for ANY omega: every term of the PRF
+    estimator equals exp(-|x|^2)/m ([P1] key formulas; the |x+y| -> 0 limit of
+    Lemma 2 in [P1] Theoretical bounds).  Catches a dropped or mis-signed
+    |x|^2/2 term and a wrong 1/sqrt(m) factor."""
+    rng = _rng(m * 100 + d)
+    omega = rng.standard_normal((m, d)) * rng.uniform(0.2, 3.0, size=(m, 1))
+    x = rng.standard_normal((9, d)) * 0.7
+    f = ref.features if impl == "numpy" else native.features
+    got = np.sum(f(x, omega) * f(-x, omega), axis=-1)
+    want = np.exp(-np.sum(x * x, axis=-1))
+    np.testing.assert_allclose(got, want, rtol=1e-13)
+
+
+@pytest.mark.parametrize("impl", ["numpy", "c"])
+def test_feature_hand_values(impl):
+    """Hand-worked feature values.  omega rows (1,0,0) and (0,2,0), x=(1,0,0):
+    omega_1.x = 1, omega_2.x = 0, |x|^2/2 = 1/2, m = 2, so
+    phi = (e^{1/2}, e^{-1/2}) / sqrt(2).  A transposed omega gives different
+    numbers (and a shape error for m != d)."""
+    omega = np.array([[1.0, 0.0, 0.0], [0.0, 2.0, 0.0]])
+    x = np.array([[1.0, 0.0, 0.0]])
+    f = ref.features if impl == "numpy" else native.features
+    got = f(x, omega)[0]
+    want = np.array([math.exp(0.5), math.exp(-0.5)]) / math.sqrt(2.0)
+    np.testing.assert_allclose(got, want, rtol=1e-14)
+    # x = (0, 1, 1): omega_1.x = 0, omega_2.x = 2, |x|^2/2 = 1
+    got2 = f(np.array([[0.0, 1.0, 1.0]]), omega)[0]
+    np.testing.assert_allclose(got2, np.array([math.exp(-1.0), math.exp(1.0)]) / math.sqrt(2.0), rtol=1e-14)
+
+
+def test_stabilized_features_scale():
+    """The stabilised features differ from the plain ones by the reported
+    per-row factor exp(s), and their largest entry is m^-1/2."""
+    rng = _rng(5)
+    omega = rng.standard_normal((24, 8))
+    x = rng.standard_normal((11, 8)) * 2.0
+    phi = ref.features(x, omega)
+    phs, s = ref.features_stabilized(x, omega)
+    np.testing.assert_allclose(phs * np.exp(s)[:, None], phi, rtol=1e-12)
+    np.testing.assert_allclose(phs.max(axis=1), 1.0 / math.sqrt(24), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Estimator statistics: Theorem 1, Lemma 2, Theorem 2
+# ---------------------------------------------------------------------------
+
+def _pair(seed, d, sq):
+    """x, y with |x+y|^2 = sq (kept <= 1 so the estimator's 4th moment is tame)."""
+    rng = _rng(seed)
+    x = rng.standard_normal(d)
+    y = rng.standard_normal(d)
+    f = math.sqrt(sq) / np.linalg.norm(x + y)
+    return x * f, y * f
+
+
+def _iid_errors(x, y, m, R, seed, chunk=20000):
+    rng = _rng(seed)
+    d = x.shape[0]
+    out = []
+    for c in range(0, R, chunk):
+        n = min(chunk, R - c)
+        om = rng.standard_normal((n, m, d))
+        out.append(ref.sm_hat(x, y, om) - math.exp(float(x @ y)))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("sq,m", [(0.5, 1), (0.5, 8), (1.0, 8)])
+def test_unbiased_and_lemma2_mse(sq, m):
+    """i.i.d. PRF estimator: mean equals exp(x.y) (Theorem 1, [P1]
+    Theoretical bounds) and the mean squared error equals the closed form
+    (1/m) exp(|x+y|^2) SM^2 (1 - exp(-|x+y|^2)) (Lemma 2, [P1] Theoretical
+    bounds and key formulas), each within 5 standard errors."""
+    d = 16
+    x, y = _pair(11 + m, d, sq)
+    R = 100000
+    e = _iid_errors(x, y, m, R, seed=1000 + m)
+    se_mean = e.std() / math.sqrt(R)
+    assert abs(e.mean()) < 5 * se_mean
+    sq_err = e * e
+    se_mse = sq_err.std() / math.sqrt(R)
+    assert abs(sq_err.mean() - ref.lemma2_mse(x, y, m)) < 5 * se_mse
+
+
+def test_lemma2_limit_zero():
+    """Lemma 2 gives MSE 0 when x + y = 0; the estimator is then exact for
+    every draw (see also the deterministic identity test)."""
+    x = np.array([0.3, -0.2, 0.5, 0.1])
+    assert ref.lemma2_mse(x, -x, 8) == 0.0
+    om = _rng(3).standard_normal((50, 8, 4))
+    np.testing.assert_allclose(ref.sm_hat(x, -x, om), math.exp(-float(x @ x)), rtol=1e-13)
+
+
+@pytest.mark.parametrize("m", [16, 32])
+def test_orf_variance_below_iid(m):
+    """Orthogonal features: still unbiased, and their MSE is strictly below
+    the i.i.d. one (Theorem 2: [P1] Theoretical bounds; [P3] section 3 and
+    F.4.1).  d = 16: m = 16 is one full block, m = 32 two independent blocks."""
+    d = 16
+    x, y = _pair(77, d, 1.0)
+    R = 40000
+    rng = _rng(2024 + m)
+    nb = (m + d - 1) // d
+    om_orf = ref.orf_from_gaussians(rng.standard_normal((R, nb, d, d)), rng.standard_normal((R, nb, d, d)), m)
+    e_orf = ref.sm_hat(x, y, om_orf) - math.exp(float(x @ y))
+    e_iid = _iid_errors(x, y, m, R, seed=4048 + m)
+    assert abs(e_orf.mean()) < 5 * e_orf.std() / math.sqrt(R)
+    diff = e_orf ** 2 - e_iid ** 2
+    assert diff.mean() < -3 * diff.std() / math.sqrt(R)
+
+
+# ---------------------------------------------------------------------------
+# Orthogonal projections and the counter-based generator
+# ---------------------------------------------------------------------------
+
+def test_philox_matches_numpy_library():
+    """The oracle's Philox4x64-10 equals numpy's ``Philox`` bit generator (the
+    same published generator; numpy advances the counter by one before each
+    block, so counter c here is numpy's c - 1)."""
+    for key in [(0, 0), (5, 7), (2 ** 64 - 1, 123456789)]:
+        for ctr0 in [0, 1, 77, 2 ** 40]:
+            bg = np.random.Philox(counter=ctr0, key=np.array(key, dtype=np.uint64))
+            want = bg.random_raw(8)
+            got = ref.philox4x64_10(np.array([[ctr0 + 1, 0, 0, 0], [ctr0 + 2, 0, 0, 0]], dtype=np.uint64), key)
+            assert np.array_equal(got.reshape(-1), want)
+    # higher counter words: numpy's 256-bit counter [c0, c1, c2, c3]
+    bg = np.random.Philox(counter=[5, 9, 3, 1], key=[42, 0])
+    want = bg.random_raw(4)
+    got = ref.philox4x64_10(np.array([6, 9, 3, 1], dtype=np.uint64), (42, 0))
+    assert np.array_equal(got, want)
+
+
+def test_philox_normals_distribution():
+    """Box-Muller normals from the generator are N(0, 1) (Kolmogorov-Smirnov
+    against scipy's normal CDF, plus the first four moments)."""
+    from scipy import stats
+    z = ref.philox_normals(7, (3, 1, 0), 200001)
+    assert z.shape == (200001,)
+    assert stats.kstest(z, "norm").pvalue > 1e-3
+    n = z.size
+    assert abs(z.mean()) < 5 / math.sqrt(n)
+    assert abs(z.var() - 1.0) < 5 * math.sqrt(2.0 / n)
+    assert abs(np.mean(z ** 4) - 3.0) < 5 * math.sqrt(96.0 / n)
+
+
+@pytest.mark.parametrize("m,d", [(16, 16), (40, 16), (256, 64), (10, 4)])
+def test_orf_structure(m, d):
+    """Rows inside each d x d block are mutually orthogonal; blocks are
+    independent, so rows of different blocks are not ([P1] core components:
+    Gram-Schmidt on the rows; block-wise when m > d).  Deterministic per seed."""
+    om = ref.orf_omega(3, 2, m, d).astype(np.float64)
+    assert om.shape == (2, m, d)
+    assert np.array_equal(om, ref.orf_omega(3, 2, m, d).astype(np.float64))
+    assert not np.array_equal(om[0], om[1])
+    for h in range(2):
+        for b0 in range(0, m, d):
+            blk = om[h, b0:b0 + d]
+            unit = blk / np.linalg.norm(blk, axis=1, keepdims=True)
+            gram = unit @ unit.T
+            off = gram - np.diag(np.diag(gram))
+            assert np.abs(off).max() < 2e-6
+    if m > d:
+        unit = om[0] / np.linalg.norm(om[0], axis=1, keepdims=True)
+        assert np.abs(unit[0] @ unit[d:].T).max() > 1e-3
+
+
+def test_orf_marginals():
+    """Each row is marginally N(0, I_d) ([P3] A.2: orthogonal features keep the
+    marginals): squared row lengths are chi-square(d) (mean d, variance 2d) and
+    entries have mean 0 and variance 1, over many seeds."""
+    d, m = 8, 16
+    rows = np.concatenate([ref.orf_omega(s, 1, m, d)[0] for s in range(600)]).astype(np.float64)
+    n = rows.shape[0]
+    sq = np.sum(rows ** 2, axis=1)
+    assert abs(sq.mean() - d) < 5 * math.sqrt(2 * d / n)
+    assert abs(sq.var() - 2 * d) < 0.15 * 2 * d
+    ent = rows.reshape(-1)
+    assert abs(ent.mean()) < 5 / math.sqrt(ent.size)
+    assert abs(ent.var() - 1.0) < 0.05
+
+
+def test_gram_schmidt_against_qr():
+    """Row-wise Gram-Schmidt equals the (sign-fixed) Q factor of the QR
+    decomposition of the transposed block (numpy's LAPACK routine)."""
+    g = _rng(9).standard_normal((6, 6))
+    u = ref.gram_schmidt_rows(g)
+    q, r = np.linalg.qr(g.T)
+    q = q * np.sign(np.diag(r))[None, :]
+    np.testing.assert_allclose(u, q.T, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def _qkv(seed, L, d, scale=0.5):
+    rng = _rng(seed)
+    return (rng.standard_normal((L, d)) * scale, rng.standard_normal((L, d)) * scale, rng.standard_normal((L, d)))
+
+
+@pytest.mark.parametrize("L,d,m", [(1, 2, 1), (2, 4, 3), (3, 2, 8), (17, 4, 8), (64, 16, 32)])
+def test_causal_equals_masked_brute_force(L, d, m):
+    """Prefix-sum recurrence = explicit lower-triangular L x L evaluation with
+    the same features ([P1] Methods and core components; [P3] section 2 and
+    A.2); the bidirectional form = the unmasked L x L evaluation
+    (associativity, [P1] atomic insights).  Both oracles."""
+    q, k, v = _qkv(L * 1000 + d * 10 + m, L, d)
+    om = _rng(m).standard_normal((m, d))
+    bf_c = ref.brute_force(q, k, v, om, causal_mask=True)
+    bf_b = ref.brute_force(q, k, v, om, causal_mask=False)
+    Q, K, V = (a[None, None] for a in (q, k, v))
+    np.testing.assert_allclose(ref.causal(Q, K, V, om)[0, 0], bf_c, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(native.causal(Q, K, V, om)[0, 0], bf_c, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ref.bidir(Q, K, V, om)[0, 0], bf_b, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(native.bidir(Q, K, V, om)[0, 0], bf_b, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_special_cases():
+    """Exact special cases: the first causal row attends to one key only, so
+    it is v_0; the last causal row is the last bidirectional row; constant V
+    rows give out = V; jointly permuting (K, V) leaves the bidirectional output
+    unchanged; permuting Q permutes the output rows."""
+    L, d, m = 23, 8, 16
+    q, k, v = _qkv(4, L, d)
+    om = ref.orf_omega(1, 1, m, d)[0]
+    Q, K, V = (a[None, None] for a in (q, k, v))
+    c = ref.causal(Q, K, V, om)[0, 0]
+    b = ref.bidir(Q, K, V, om)[0, 0]
+    np.testing.assert_allclose(c[0], v[0], rtol=1e-13)
+    np.testing.assert_allclose(c[-1], b[-1], rtol=1e-12)
+    const = np.tile(np.arange(d, dtype=np.float64), (L, 1))
+    np.testing.assert_allclose(ref.bidir(Q, K, const[None, None], om)[0, 0], const, rtol=1e-12)
+    np.testing.assert_allclose(ref.causal(Q, K, const[None, None], om)[0, 0], const, rtol=1e-12)
+    p = _rng(8).permutation(L)
+    np.testing.assert_allclose(ref.bidir(Q, K[:, :, p], V[:, :, p], om)[0, 0], b, rtol=1e-12)
+    np.testing.assert_allclose(ref.bidir(Q[:, :, p], K, V, om)[0, 0], b[p], rtol=1e-12)
+
+
+def test_scale_invariance():
+    """A per-row factor on query features and one common factor on all key
+    features leave the normalised output unchanged ([P2] Simple Derivation);
+    this is what licenses the GPU's stabilisers."""
+    L, d, m = 31, 8, 24
+    q, k, v = _qkv(12, L, d, scale=1.5)
+    om = _rng(2).standard_normal((m, d))
+    pq, _ = ref.features_stabilized(q, om)
+    pk = ref.features(k, om) * math.exp(-7.5)
+    a = np.tril(pq @ pk.T)
+    out = (a @ v) / a.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(out, ref.brute_force(q, k, v, om, causal_mask=True), rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal_mask", [False, True])
+def test_softmax_attention_matches_torch(causal_mask):
+    """The exact-softmax target equals torch's scaled_dot_product_attention
+    (fp64, CPU) with scale 1 (the kernel is exp(q.k), [P1] Methods)."""
+    q, k, v = _qkv(21, 40, 8, scale=0.8)
+    t = [torch.from_numpy(a)[None, None] for a in (q, k, v)]
+    want = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=causal_mask, scale=1.0)[0, 0].numpy()
+    np.testing.assert_allclose(ref.softmax_attention(q, k, v, causal_mask), want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal_mask", [False, True])
+def test_monte_carlo_convergence_to_softmax(causal_mask):
+    """FAVOR+ with orthogonal features converges to exact softmax attention as
+    m grows (Theorem 1 and uniform convergence, [P1] Theoretical bounds; the
+    L = 4096, d = 16 approximation study of [P3] section 3, here at L = 256).
+
+    Lemma 2 puts the per-entry variance at exp(|q+k|^2)/m, so the Monte-Carlo
+    rate m^-1/2 shows once m >> exp(|q+k|^2): with entries of q, k at 0.25
+    (|q+k|^2 about 2) the median error over seeds must fall at a log-log slope
+    near -1/2.  At the workloads' d^-1/4 scale (|q+k|^2 about 8) the error must
+    still fall from m = 256 to m = 16384."""
+    L, d = 256, 16
+    ms = [64, 256, 1024, 4096, 16384]
+
+    def medians(sigma, seeds):
+        rng = _rng(0)
+        q = rng.standard_normal((L, d)) * sigma
+        k = rng.standard_normal((L, d)) * sigma
+        v = rng.standard_normal((L, d))
+        exact = ref.softmax_attention(q, k, v, causal_mask)
+        med = []
+        for m in ms:
+            errs = []
+            for s in range(seeds):
+                g = _rng(100 * m + s).standard_normal((2, (m + d - 1) // d, d, d))
+                approx = ref.brute_force(q, k, v, ref.orf_from_gaussians(g[0], g[1], m), causal_mask)
+                errs.append(np.linalg.norm(approx - exact) / np.linalg.norm(exact))
+            med.append(float(np.median(errs)))
+        return med
+
+    med = medians(0.25, 8)
+    assert all(med[i + 1] < med[i] for i in range(len(ms) - 1))
+    slope = (math.log(med[-1]) - math.log(med[1])) / (math.log(ms[-1]) - math.log(ms[1]))
+    assert -0.65 < slope < -0.35
+    assert med[-1] < 0.05
+    med_w = medians(d ** -0.25, 4)
+    assert med_w[-1] < 0.75 * med_w[1]
+
+
+def test_rows_helpers_match_full():
+    """Single-row evaluations used for long sequences equal the full oracle."""
+    L, d, m = 50, 8, 16
+    q, k, v = _qkv(3, L, d)
+    om = ref.orf_omega(0, 1, m, d)[0]
+    Q, K, V = (a[None, None] for a in (q, k, v))
+    rows = np.array([0, 1, 17, 49])
+    np.testing.assert_allclose(ref.causal_rows(q, k, v, om, rows), ref.causal(Q, K, V, om)[0, 0, rows], rtol=1e-12)
+    np.testing.assert_allclose(ref.bidir_rows(q, k, v, om, rows), ref.bidir(Q, K, V, om)[0, 0, rows], rtol=1e-12)
+
+
+def test_c_and_numpy_oracles_agree_multihead():
+    """The plain-C and numpy oracles agree on multi-batch, multi-head inputs
+    with per-head and shared omega."""
+    rng = _rng(31)
+    B, H, L, d, m = 2, 3, 45, 16, 40
+    q, k, v = (rng.standard_normal((B, H, L, d)) * s for s in (0.5, 0.5, 1.0))
+    for om in (ref.orf_omega(2, H, m, d), ref.orf_omega(2, 1, m, d)[0]):
+        np.testing.assert_allclose(native.bidir(q, k, v, om), ref.bidir(q, k, v, om), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(native.causal(q, k, v, om), ref.causal(q, k, v, om), rtol=1e-11, atol=1e-12)
