@@ -1,0 +1,135 @@
+/*
+ * favor.h — C ABI of the MI355X (gfx950) FAVOR+ attention library.
+ *
+ * FAVOR+ ("Fast Attention Via positive Orthogonal Random features") replaces
+ * the softmax kernel exp(q.k) by an inner product of positive random features
+ *     phi(x)_i = m^-1/2 exp(omega_i . x - |x|^2 / 2),   i = 1..m,
+ * over a projection Omega in R^{m x d} with orthogonal Gaussian rows, and
+ * evaluates attention by associativity, never forming the L x L matrix.
+ * Pages: "Performer — 랜덤 특징으로 어텐션을 다시 생각하기" (digest of
+ * *Rethinking Attention with Performers*, irregular6612.github.io), sections
+ * "Methods (FAVOR+)", core components and key formulas; Su Jianlin, "From
+ * Performer to Linear Attention", Simple Derivation; paperlayer.ai summary of
+ * arXiv:2009.14794v4, sections 2, A.2 and B.3.
+ *
+ * Conventions for every entry point below:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, contiguous,
+ *     row-major.  q, k, v, out (and x) are [B, H, L, d]; omega is fp32 and is
+ *     either [m, d] (omega_head_stride = 0: one projection for all heads) or
+ *     [H, m, d] (omega_head_stride = m*d: one per head); every batch element
+ *     uses the same projection, and queries and keys of a head share it.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream);
+ *     nothing synchronises, nothing allocates device memory, no global
+ *     mutable state is kept: calls are re-entrant and thread-safe.
+ *   - The return value reports argument validation (done before any HIP call)
+ *     and launch errors.  Device faults surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this interface.
+ *   - Accumulation is fp32.  bf16 inputs give bf16 outputs.  There is no
+ *     temperature: the library computes exp(q.k) exactly as defined; callers
+ *     wanting softmax(q.k / sqrt(d)) pre-scale q and k by d^-1/4.
+ *   - Supported: d in {16, 32, 64, 128}; m a multiple of 32, 32 <= m <= 512;
+ *     B, H >= 1; L >= 0 (L = 0 is a no-op); B*H*L*d < 2^31.
+ */
+#ifndef FAVOR_H_
+#define FAVOR_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FAVOR_F32 = 0, FAVOR_BF16 = 1 } favor_dtype;
+
+typedef enum {
+    FAVOR_OK = 0,
+    FAVOR_ERR_INVALID_ARG = 1, /* null pointer, bad dimension, out aliasing an input  */
+    FAVOR_ERR_UNSUPPORTED = 2, /* d, m or dtype outside the supported set             */
+    FAVOR_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required     */
+    FAVOR_ERR_HIP = 4          /* a HIP launch failed (hipGetLastError after launch)   */
+} favor_status;
+
+typedef struct {
+    int B, H, L, d, m;           /* q, k, v, out: [B, H, L, d]; m random features        */
+    favor_dtype dtype;           /* element type of q, k, v, out, x                      */
+    long long omega_head_stride; /* 0: omega is [m, d]; m*d: omega is [H, m, d]          */
+} favor_shape;
+
+/* Operation codes for favor_workspace_bytes. */
+#define FAVOR_OP_FEATURES 0
+#define FAVOR_OP_BIDIR 1
+#define FAVOR_OP_CAUSAL 2
+
+/*
+ * Bytes of device workspace the given operation needs for this shape.
+ * `chunk` is the causal chunk length (0 = default) and is ignored otherwise.
+ * Returns 0 for an invalid or unsupported shape (the operation itself reports
+ * which).  The size depends only on the shape, never on the device.
+ */
+size_t favor_workspace_bytes(int op, const favor_shape *shape, int chunk);
+
+/*
+ * Positive random features of x ([B, H, L, d]) into phi ([B, H, L, m], fp32):
+ *     phi_i = m^-1/2 exp(omega_i . x - |x|^2/2 - s)
+ * ("Performer" digest, core components: the positive random feature map).
+ * stabilize = 0: s = 0 and log_scale may be NULL.
+ * stabilize = 1: s = max_i(omega_i . x - |x|^2/2) per row, written to
+ *                log_scale ([B, H, L] fp32, natural-log units), so that the
+ *                unstabilised features are phi * exp(log_scale).
+ * The projection uses omega rounded to the input dtype (bf16 inputs: bf16
+ * omega * log2(e), fp32 accumulation).  ws/ws_bytes: device workspace of at
+ * least favor_workspace_bytes(FAVOR_OP_FEATURES, shape, 0) bytes, 256-byte
+ * aligned.  phi must not overlap x; log_scale must not overlap phi.
+ */
+favor_status favor_features(const favor_shape *shape, const void *x, const float *omega, float *phi,
+                            float *log_scale, int stabilize, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Bidirectional FAVOR+ ("Performer" digest, key formulas and method
+ * flowchart):
+ *     out_t = phi(q_t)^T (sum_s phi(k_s) v_s^T) / phi(q_t)^T (sum_s phi(k_s)).
+ * ws/ws_bytes: device workspace of at least
+ * favor_workspace_bytes(FAVOR_OP_BIDIR, shape, 0) bytes, 256-byte aligned;
+ * its contents need not be initialised and are garbage afterwards.
+ * out must not overlap q, k, v or ws.
+ */
+favor_status favor_bidir(const favor_shape *shape, const void *q, const void *k, const void *v,
+                         const float *omega, void *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Causal (unidirectional) FAVOR+ by prefix sums ("Performer" digest, Methods:
+ * G_t = sum_{s<=t} phi(k_s) v_s^T; paperlayer.ai summary, A.2 unidirectional
+ * attention):
+ *     out_t = phi(q_t)^T G_t / phi(q_t)^T (sum_{s<=t} phi(k_s)),
+ * with an inclusive mask (position t attends to keys 0..t).
+ * chunk: tokens per step of the chunked scan (0 = default 32; allowed 32).
+ * Workspace as for favor_bidir with FAVOR_OP_CAUSAL.
+ */
+favor_status favor_causal(const favor_shape *shape, const void *q, const void *k, const void *v,
+                          const float *omega, void *out, int chunk, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/*
+ * Seeded orthogonal random projection, written to HOST memory
+ * omega_host[n_heads, m, d] (fp32), computed on the CPU.  For each head,
+ * ceil(m/d) independent blocks: a d x d Gaussian whose rows are
+ * orthonormalised by Gram-Schmidt in row order, each row then scaled to the
+ * length of an independent N(0, I_d) vector, so rows are marginally
+ * N(0, I_d) ("Performer" digest, core components: Gram-Schmidt on the rows,
+ * block-wise when m > d; paperlayer.ai summary, A.2: marginals preserved).
+ * Gaussians come from Philox4x64-10 (Salmon et al., SC'11) with key
+ * (seed, 0): block b of head h reads counter (j, b, h, 0) for the matrix and
+ * (j, b, h, 1) for the lengths, four normals per counter via Box-Muller on
+ * 53-bit uniforms u = ((w >> 11) + 1) 2^-53.
+ * Returns FAVOR_ERR_INVALID_ARG for a null pointer or non-positive size.
+ */
+favor_status favor_orf_omega(unsigned long long seed, int n_heads, int m, int d, float *omega_host);
+
+/* Static, human-readable name of a status code. */
+const char *favor_status_string(favor_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAVOR_H_ */

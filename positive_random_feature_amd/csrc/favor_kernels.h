@@ -1,0 +1,48 @@
+// Internal interface between the C ABI (favor_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace favor {
+
+// LDS available to one workgroup on gfx950.
+constexpr size_t kMaxLds = 160 * 1024;
+
+enum class OpKind { Features, Bidir, Causal };
+
+struct LaunchArgs {
+    OpKind op;
+    int dtype_bytes;  // 2 = bf16, 4 = fp32
+    int B, H, L, D, m;
+    bool omega_per_head;
+    const void *q, *k, *v;  // for Features, q is x
+    const float* omega;
+    void* out;
+    float* phi;
+    float* log_scale;
+    int stabilize;
+    int nseg, seg_len;  // segments per head and their length (multiple of 32)
+    // workspace regions
+    void* ws_ompack;
+    float* ws_partial;
+    float* ws_pmax;
+    void* ws_kvpack;
+    float* ws_mmax;
+    float* ws_carry;
+    float* ws_cmax;
+    hipStream_t stream;
+};
+
+struct CausalCfg {
+    int fw;    // features per wave
+    int maxw;  // waves per workgroup the kernel is compiled for
+    int w;     // waves per workgroup = m / fw (0: unsupported)
+};
+
+hipError_t launch(const LaunchArgs& a);
+CausalCfg causal_config(int D, int m);
+// LDS bytes the causal kernel needs (SIZE_MAX when the shape is unsupported).
+size_t causal_smem_bytes(int dtype_bytes, int D, int m);
+
+}  // namespace favor

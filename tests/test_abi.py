@@ -1,0 +1,126 @@
+"""C-ABI contract tests that run without a GPU: the library loads, exports
+every entry point the header declares, validates arguments before any HIP
+call, and its host-side projection generator matches the oracle's."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.reference as ref
+from positive_random_feature_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+# fake, 256-byte-aligned device addresses: validation rejects the call before
+# any of them is touched
+P_Q, P_K, P_V, P_O, P_OM, P_WS = (0x10000000 * (i + 1) for i in range(6))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from positive_random_feature_amd import build
+        build.build()
+    return _lib.load()
+
+
+def shp(B=1, H=2, L=64, d=64, m=256, dtype=_lib.FAVOR_BF16, stride=0):
+    return _lib.shape(B, H, L, d, m, dtype, stride)
+
+
+def test_exports_every_declared_symbol(lib):
+    header = open(os.path.join(ROOT, "include", "favor.h")).read()
+    names = set(re.findall(r"\b(favor_[a-z_]+)\s*\(", header))
+    assert {"favor_features", "favor_bidir", "favor_causal", "favor_workspace_bytes", "favor_orf_omega",
+            "favor_status_string"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.favor_status_string(code)
+    assert lib.favor_status_string(0) == b"ok"
+
+
+def test_workspace_bytes(lib):
+    s = shp()
+    for op in (0, 1, 2):
+        assert lib.favor_workspace_bytes(op, ctypes.byref(s), 0) > 0
+    assert lib.favor_workspace_bytes(7, ctypes.byref(s), 0) == 0
+    assert lib.favor_workspace_bytes(1, ctypes.byref(shp(d=48)), 0) == 0
+    assert lib.favor_workspace_bytes(1, None, 0) == 0
+    # grows with the number of heads
+    assert lib.favor_workspace_bytes(2, ctypes.byref(shp(H=8)), 0) > lib.favor_workspace_bytes(2, ctypes.byref(s), 0)
+
+
+def _bidir(lib, s, q=P_Q, k=P_K, v=P_V, om=P_OM, o=P_O, ws=P_WS, nbytes=1 << 40):
+    return lib.favor_bidir(ctypes.byref(s) if s is not None else None, q, k, v, om, o, ws, nbytes, None)
+
+
+def _causal(lib, s, chunk=0, q=P_Q, k=P_K, v=P_V, om=P_OM, o=P_O, ws=P_WS, nbytes=1 << 40):
+    return lib.favor_causal(ctypes.byref(s) if s is not None else None, q, k, v, om, o, chunk, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("fn", [_bidir, _causal])
+def test_validation(lib, fn):
+    assert fn(lib, None) == INVALID
+    assert fn(lib, shp(B=0)) == INVALID
+    assert fn(lib, shp(H=-1)) == INVALID
+    assert fn(lib, shp(L=-5)) == INVALID
+    assert fn(lib, shp(d=48)) == UNSUPPORTED
+    assert fn(lib, shp(d=256)) == UNSUPPORTED
+    assert fn(lib, shp(m=33)) == UNSUPPORTED
+    assert fn(lib, shp(m=544)) == UNSUPPORTED
+    assert fn(lib, shp(m=288)) == UNSUPPORTED
+    assert fn(lib, shp(dtype=7)) == UNSUPPORTED
+    assert fn(lib, shp(stride=5)) == INVALID
+    assert fn(lib, shp(), q=None) == INVALID
+    assert fn(lib, shp(), om=None) == INVALID
+    assert fn(lib, shp(), o=None) == INVALID
+    assert fn(lib, shp(), q=P_Q + 8) == INVALID          # 16-byte alignment
+    assert fn(lib, shp(), o=P_Q) == INVALID              # out aliases q
+    assert fn(lib, shp(), o=P_V + 64) == INVALID         # out overlaps v
+    assert fn(lib, shp(), ws=None) == WORKSPACE
+    assert fn(lib, shp(), ws=P_WS + 16) == WORKSPACE     # 256-byte alignment
+    need = lib.favor_workspace_bytes(1 if fn is _bidir else 2, ctypes.byref(shp()), 0)
+    assert fn(lib, shp(), nbytes=need - 1) == WORKSPACE
+    assert fn(lib, shp(L=0), q=None, k=None, v=None, o=None, ws=None, nbytes=0) == OK  # L = 0: no-op
+    assert fn(lib, shp(B=1 << 16, H=1 << 8, L=1 << 8, d=64)) == UNSUPPORTED            # > 2^31 elements
+
+
+def test_causal_chunk_and_lds_limits(lib):
+    assert _causal(lib, shp(), chunk=64) == UNSUPPORTED
+    assert _causal(lib, shp(), chunk=-1) == UNSUPPORTED
+    # fp32 d=128 m=512: the causal state does not fit one workgroup's LDS
+    assert _causal(lib, shp(d=128, m=512, dtype=_lib.FAVOR_F32)) == UNSUPPORTED
+
+
+def test_features_validation(lib):
+    s = shp()
+    f = lib.favor_features
+    assert f(ctypes.byref(s), None, P_OM, P_O, None, 0, P_WS, 1 << 40, None) == INVALID
+    assert f(ctypes.byref(s), P_Q, P_OM, P_O, None, 1, P_WS, 1 << 40, None) == INVALID   # log_scale needed
+    assert f(ctypes.byref(s), P_Q, P_OM, P_Q, None, 0, P_WS, 1 << 40, None) == INVALID   # phi overlaps x
+    assert f(ctypes.byref(s), P_Q, P_OM, P_O, None, 0, P_WS, 16, None) == WORKSPACE
+
+
+@pytest.mark.parametrize("seed,H,m,d", [(0, 1, 32, 16), (0, 8, 256, 64), (3, 2, 40, 16), (11, 1, 512, 128), (5, 3, 10, 4)])
+def test_orf_omega_matches_oracle(lib, seed, H, m, d):
+    """The library's host generator (same published Philox4x64-10 and the same
+    construction) reproduces the oracle's projection."""
+    out = np.empty((H, m, d), dtype=np.float32)
+    assert lib.favor_orf_omega(seed, H, m, d, out.ctypes.data) == OK
+    want = ref.orf_omega(seed, H, m, d)
+    np.testing.assert_allclose(out, want, rtol=2e-7, atol=2e-7)
+
+
+def test_orf_omega_invalid(lib):
+    out = np.empty(16, dtype=np.float32)
+    assert lib.favor_orf_omega(0, 1, 4, 4, None) == INVALID
+    assert lib.favor_orf_omega(0, 0, 4, 4, out.ctypes.data) == INVALID
+    assert lib.favor_orf_omega(0, 1, -4, 4, out.ctypes.data) == INVALID

@@ -1,0 +1,254 @@
+"""GPU parity: the HIP library through the C ABI against the fp64 CPU oracle
+on the same seeded inputs and projection.
+
+Bar (relative L2 over the compared outputs): 1e-5 for fp32 inputs, 2e-2 for
+bf16 inputs with fp32 accumulation.  Small cases compare every element and
+span several 32-token tiles, segments and ragged tails; the five workloads
+run at their full sizes (the longest causal one on sampled rows the oracle
+computes one by one).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.native as native
+import oracle.reference as ref
+import positive_random_feature_amd as favor
+from positive_random_feature_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def _dev():
+    return torch.device("cuda:0")
+
+
+def _to_dev(inp, dtype):
+    if dtype == "bf16":
+        return [torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(_dev()) for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
+    return [torch.from_numpy(a).to(_dev()) for a in (inp.q, inp.k, inp.v)]
+
+
+def _omega(w, H, seed=None):
+    om = ref.orf_omega(w.seed if seed is None else seed, H if w.omega_per_head else 1, w.m, w.d)
+    return om if w.omega_per_head else om[0]
+
+
+def _rel(got, want):
+    return float(np.linalg.norm(got - want) / np.linalg.norm(want))
+
+
+def _run(w, op, B, H, L, seed=None, omega=None):
+    inp = make_inputs(w, B=B, H=H, L=L, seed=seed)
+    om = _omega(w, H) if omega is None else omega
+    q, k, v = _to_dev(inp, w.dtype)
+    fn = favor.bidir if op == "bidir" else favor.causal
+    out = fn(q, k, v, torch.from_numpy(om).to(_dev()))
+    torch.cuda.synchronize()
+    return inp, om, out.float().cpu().numpy().astype(np.float64)
+
+
+def _log(name, err, tol):
+    print(f"[parity] {name}: rel L2 {err:.3e} (tol {tol})", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# small and ragged cases: every element
+# ---------------------------------------------------------------------------
+
+SMALL = [(1, 1, 1), (1, 2, 2), (2, 1, 31), (1, 2, 32), (1, 3, 33), (2, 2, 97), (1, 1, 300), (1, 2, 1000)]
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("op", ["bidir", "causal"])
+@pytest.mark.parametrize("B,H,L", SMALL)
+def test_small_every_element(name, op, B, H, L):
+    w = WORKLOADS[name]
+    inp, om, got = _run(w, op, B, H, L)
+    want = (native.bidir if op == "bidir" else native.causal)(inp.q, inp.k, inp.v, om)
+    err = _rel(got, want)
+    _log(f"{name} {op} B={B} H={H} L={L}", err, TOL[w.dtype])
+    assert np.isfinite(got).all()
+    assert err <= TOL[w.dtype]
+
+
+def test_causal_first_row_is_first_value():
+    """Position 0 attends to key 0 only, so its output is v_0 (up to output
+    rounding), on every head."""
+    w = WORKLOADS["causal_bf16_8k"]
+    inp, om, got = _run(w, "causal", 2, 3, 130)
+    np.testing.assert_allclose(got[:, :, 0], inp.v[:, :, 0], rtol=1e-2, atol=1e-2)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["bidir_f32_tiny", "bidir_bf16_4k", "bidir_bf16_12k"])
+def test_workload_bidir_full(name):
+    w = WORKLOADS[name]
+    inp, om, got = _run(w, "bidir", w.B, w.H, w.L)
+    want = ref.bidir(inp.q, inp.k, inp.v, om)
+    err = _rel(got, want)
+    _log(f"{name} full", err, TOL[w.dtype])
+    assert err <= TOL[w.dtype]
+
+
+def test_workload_tiny_causal_full():
+    w = WORKLOADS["bidir_f32_tiny"]
+    inp, om, got = _run(w, "causal", w.B, w.H, w.L)
+    err = _rel(got, native.causal(inp.q, inp.k, inp.v, om))
+    _log("bidir_f32_tiny via causal", err, 1e-5)
+    assert err <= 1e-5
+
+
+def test_workload_causal_8k_full():
+    w = WORKLOADS["causal_bf16_8k"]
+    inp, om, got = _run(w, "causal", w.B, w.H, w.L)
+    want = native.causal(inp.q, inp.k, inp.v, om)
+    err = _rel(got, want)
+    _log("causal_bf16_8k full", err, TOL[w.dtype])
+    assert err <= TOL[w.dtype]
+    # no head is much worse than the whole
+    for b in range(w.B):
+        for h in range(w.H):
+            assert _rel(got[b, h], want[b, h]) <= TOL[w.dtype]
+
+
+def test_workload_causal_64k_sampled():
+    """Full-size long causal run (large |q||k|); the oracle evaluates sampled
+    rows of four heads one by one, including the first and last rows and
+    rows around segment boundaries."""
+    w = WORKLOADS["causal_bf16_64k"]
+    inp, om, got = _run(w, "causal", w.B, w.H, w.L)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 33, 4095, 4096, 4097, w.L - 1],
+                                     rng.integers(0, w.L, size=40)]))
+    errs = []
+    for h in (0, 5, 10, 15):
+        want = ref.causal_rows(inp.q[0, h], inp.k[0, h], inp.v[0, h], om[h], rows)
+        errs.append(_rel(got[0, h, rows], want))
+        _log(f"causal_bf16_64k head {h} sampled", errs[-1], TOL[w.dtype])
+    assert max(errs) <= TOL[w.dtype]
+
+
+# ---------------------------------------------------------------------------
+# invariances and edge cases
+# ---------------------------------------------------------------------------
+
+def test_causal_prefix_invariance():
+    """Causal outputs of a prefix do not depend on later tokens, whatever the
+    segmentation chosen for the two lengths."""
+    w = WORKLOADS["causal_bf16_8k"]
+    om = torch.from_numpy(_omega(w, 2)).to(_dev())
+    inp = make_inputs(w, B=1, H=2, L=2000)
+    q, k, v = _to_dev(inp, w.dtype)
+    full = favor.causal(q, k, v, om).float()
+    part = favor.causal(q[:, :, :700].contiguous(), k[:, :, :700].contiguous(), v[:, :, :700].contiguous(), om).float()
+    d = (full[:, :, :700] - part).norm() / part.norm()
+    assert float(d) < 1e-2
+
+
+def test_deterministic():
+    w = WORKLOADS["bidir_bf16_4k"]
+    om = torch.from_numpy(_omega(w, 2)).to(_dev())
+    inp = make_inputs(w, B=1, H=2, L=1500)
+    q, k, v = _to_dev(inp, w.dtype)
+    a = favor.bidir(q, k, v, om)
+    b = favor.bidir(q, k, v, om)
+    c1 = favor.causal(q, k, v, om)
+    c2 = favor.causal(q, k, v, om)
+    assert torch.equal(a, b) and torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("op", ["bidir", "causal"])
+def test_large_norm_stabilisers(op):
+    """Entries of q, k at 3 d^-1/4: exponents far outside exp's fp32 range
+    without shifts; the stabilised kernels still match the oracle."""
+    w = WORKLOADS["causal_bf16_8k"].replace(qk_scale=3.0)
+    inp, om, got = _run(w, op, 1, 2, 600)
+    want = (native.bidir if op == "bidir" else native.causal)(inp.q, inp.k, inp.v, om)
+    assert np.isfinite(got).all()
+    err = _rel(got, want)
+    _log(f"large-norm {op}", err, 2e-2)
+    assert err <= 2e-2
+
+
+@pytest.mark.parametrize("d,m", [(16, 32), (32, 64), (64, 96), (128, 128), (128, 256), (64, 512)])
+@pytest.mark.parametrize("op", ["bidir", "causal"])
+def test_other_shapes(d, m, op):
+    w = WORKLOADS["causal_bf16_8k"].replace(d=d, m=m)
+    inp, om, got = _run(w, op, 1, 2, 333)
+    want = (native.bidir if op == "bidir" else native.causal)(inp.q, inp.k, inp.v, om)
+    err = _rel(got, want)
+    _log(f"bf16 d={d} m={m} {op}", err, 2e-2)
+    assert err <= 2e-2
+
+
+@pytest.mark.parametrize("d,m", [(32, 64), (64, 256)])
+@pytest.mark.parametrize("op", ["bidir", "causal"])
+def test_fp32_shapes(d, m, op):
+    w = WORKLOADS["bidir_f32_tiny"].replace(d=d, m=m, omega_per_head=True)
+    inp, om, got = _run(w, op, 1, 2, 200)
+    want = (native.bidir if op == "bidir" else native.causal)(inp.q, inp.k, inp.v, om)
+    err = _rel(got, want)
+    _log(f"fp32 d={d} m={m} {op}", err, 1e-5)
+    assert err <= 1e-5
+
+
+def test_library_projection_end_to_end():
+    """The library's own projection generator feeding the GPU path gives the
+    oracle's result with the oracle's projection (the two are identical)."""
+    w = WORKLOADS["bidir_bf16_4k"]
+    inp = make_inputs(w, B=1, H=2, L=512)
+    q, k, v = _to_dev(inp, w.dtype)
+    om_lib = favor.orf_omega(0, 1, w.m, w.d)[0]
+    got = favor.bidir(q, k, v, om_lib.to(_dev())).float().cpu().numpy()
+    want = ref.bidir(inp.q, inp.k, inp.v, ref.orf_omega(0, 1, w.m, w.d)[0])
+    assert _rel(got, want) <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# features
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["bidir_f32_tiny", "bidir_bf16_4k", "causal_bf16_64k"])
+def test_features_parity(name):
+    w = WORKLOADS[name]
+    H = 2
+    inp = make_inputs(w, B=1, H=H, L=77)
+    om = _omega(w, H)
+    x = _to_dev(inp, w.dtype)[0]
+    phi, _ = favor.features(x, torch.from_numpy(om).to(_dev()))
+    got = phi.cpu().numpy().astype(np.float64)
+    oms = om if om.ndim == 3 else np.stack([om] * H)
+    want = np.stack([ref.features(inp.q[0, h], oms[h]) for h in range(H)])[None]
+    err = _rel(got, want)
+    _log(f"features {name}", err, TOL[w.dtype])
+    assert err <= TOL[w.dtype]
+    # stabilised: phi_s * exp(s) = phi, and s matches the oracle's row maximum
+    phs, ls = favor.features(x, torch.from_numpy(om).to(_dev()), stabilize=True)
+    phs = phs.cpu().numpy().astype(np.float64)
+    ls = ls.cpu().numpy().astype(np.float64)
+    assert _rel(phs * np.exp(ls)[..., None], want) <= TOL[w.dtype]
+    s_want = np.stack([ref.features_stabilized(inp.q[0, h], oms[h])[1] for h in range(H)])[None]
+    assert np.abs(ls - s_want).max() <= (1e-4 if w.dtype == "f32" else 0.05 * (1 + np.abs(s_want).max()))
+
+
+@pytest.mark.parametrize("name", ["bidir_f32_tiny", "bidir_bf16_4k"])
+def test_features_opposite_identity(name):
+    """phi(x).phi(-x) = exp(-|x|^2) for any projection, on the GPU's output."""
+    w = WORKLOADS[name]
+    inp = make_inputs(w, B=1, H=1, L=50)
+    om = torch.from_numpy(_omega(w, 1)).to(_dev())
+    x = _to_dev(inp, w.dtype)[0]
+    a, _ = favor.features(x, om)
+    b, _ = favor.features((-x).contiguous(), om)
+    got = (a.double() * b.double()).sum(-1).cpu().numpy()
+    want = np.exp(-np.sum(inp.q.astype(np.float64) ** 2, axis=-1))
+    err = _rel(got, want)
+    assert err <= TOL[w.dtype]
