@@ -1,0 +1,264 @@
+"""FAVOR+ throughput on one MI355X.
+
+One step = one bidirectional FAVOR+ pass over B=4 H=8 L=4096 (d=64, m=256,
+one shared projection) plus one causal FAVOR+ pass over B=2 H=8 L=8192 (d=64,
+m=256, one projection per head), bf16 inputs with fp32 accumulation, inputs
+resident in device memory.  The metric is tokens (B*H*L) per second over the
+whole step.
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import positive_random_feature_amd as favor  # noqa: E402
+from positive_random_feature_amd import _lib  # noqa: E402
+from positive_random_feature_amd.workloads import WORKLOADS, make_inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+STAGES = {"bidir": ["pack_omega", "kv_partial", "merge", "bidir_out"],
+          "causal": ["pack_omega", "kv_partial", "scan", "causal_chunk"]}
+KERNEL_SOURCES = ["positive_random_feature_amd/csrc/favor_kernels.hip", "positive_random_feature_amd/csrc/favor_device.h"]
+
+
+class Hip:
+    """Minimal HIP event API through ctypes (events on any stream handle)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def record(self, e, stream):
+        if self.lib.hipEventRecord(e, ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        self.lib.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+
+def to_dev_bf16(bits, dev):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class Op:
+    def __init__(self, name, dev):
+        self.w = WORKLOADS[name]
+        w = self.w
+        inp = make_inputs(w)
+        self.inp = inp
+        self.q, self.k, self.v = (to_dev_bf16(b, dev) for b in (inp.q_bits, inp.k_bits, inp.v_bits))
+        om = favor.orf_omega(w.seed, w.H if w.omega_per_head else 1, w.m, w.d)
+        self.omega_host = om.numpy() if w.omega_per_head else om[0].numpy()
+        self.omega = (om if w.omega_per_head else om[0]).contiguous().to(dev)
+        self.out = torch.empty_like(self.q)
+        self.shape = favor._shape(self.q, self.omega)
+        opcode = _lib.FAVOR_OP_BIDIR if w.op == "bidir" else _lib.FAVOR_OP_CAUSAL
+        self.ws = torch.empty(favor.workspace_bytes(opcode, self.shape), dtype=torch.uint8, device=dev)
+
+    def run(self, stream):
+        lib = _lib.load()
+        w = self.w
+        if w.op == "bidir":
+            st = lib.favor_bidir(ctypes.byref(self.shape), self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                 self.omega.data_ptr(), self.out.data_ptr(), self.ws.data_ptr(), self.ws.numel(), stream)
+        else:
+            st = lib.favor_causal(ctypes.byref(self.shape), self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                  self.omega.data_ptr(), self.out.data_ptr(), w.chunk, self.ws.data_ptr(),
+                                  self.ws.numel(), stream)
+        _lib.check(st, w.op)
+
+    def run_profiled(self, stream, events):
+        lib = _lib.load()
+        w = self.w
+        arr = (ctypes.c_void_p * len(events))(*[e.value for e in events])
+        if w.op == "bidir":
+            st = lib.favor_bidir_profiled(ctypes.byref(self.shape), self.q.data_ptr(), self.k.data_ptr(),
+                                          self.v.data_ptr(), self.omega.data_ptr(), self.out.data_ptr(),
+                                          self.ws.data_ptr(), self.ws.numel(), stream, arr, len(events))
+        else:
+            st = lib.favor_causal_profiled(ctypes.byref(self.shape), self.q.data_ptr(), self.k.data_ptr(),
+                                           self.v.data_ptr(), self.omega.data_ptr(), self.out.data_ptr(), w.chunk,
+                                           self.ws.data_ptr(), self.ws.numel(), stream, arr, len(events))
+        _lib.check(st, w.op + " (profiled)")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    entry = t.get("kernels", {}).get(kernel)
+    if not entry or t.get("source_hash") != src_hash:
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(ops):
+    """The plain-C fp64 oracle on the host cores, over one full step's inputs."""
+    from oracle import native
+    native.build(force=False)
+    t_total = 0.0
+    tokens = 0
+    for op in ops:
+        inp = op.inp
+        fn = native.bidir if op.w.op == "bidir" else native.causal
+        t0 = time.perf_counter()
+        fn(inp.q, inp.k, inp.v, op.omega_host)
+        t_total += time.perf_counter() - t0
+        tokens += op.w.tokens
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": native.num_threads(), "kind": "oracle",
+            "sample": "one full step: bidir 4x8x4096 + causal 2x8x8192 (d=64, m=256), fp64 plain-C oracle, "
+                      "OpenMP over heads", "seconds": t_total}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 512 MiB device copy first (calibrates HBM counters in profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = Hip()
+    ops = [Op("bidir_bf16_4k", dev), Op("causal_bf16_8k", dev)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    tokens_per_step = sum(op.w.tokens for op in ops)
+
+    if args.calib_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for op in ops:
+            op.run(stream)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    hip.record(e0, stream)
+    for _ in range(args.steps):
+        for op in ops:
+            op.run(stream)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = hip.elapsed_ms(e0, e1)
+    ms_per_step = ms_total / args.steps
+
+    # stage-timed region: the same K steps with events between kernels
+    n_ev = _lib.FAVOR_N_STAGES + 1
+    evs = [[[hip.event() for _ in range(n_ev)] for _ in ops] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        for i, op in enumerate(ops):
+            op.run_profiled(stream, evs[s][i])
+    torch.cuda.synchronize()
+    stage_ms = {}
+    op_ms = {}
+    for i, op in enumerate(ops):
+        per_stage = np.zeros(_lib.FAVOR_N_STAGES)
+        for s in range(args.steps):
+            for j in range(_lib.FAVOR_N_STAGES):
+                per_stage[j] += hip.elapsed_ms(evs[s][i][j], evs[s][i][j + 1])
+        per_stage /= args.steps
+        for j, name in enumerate(STAGES[op.w.op]):
+            stage_ms[f"{op.w.name}:{name}"] = float(per_stage[j])
+        op_ms[op.w.name] = float(per_stage.sum())
+
+    # dominant kernel and its roofline (HBM-bound: m = 256 < the bf16 ridge)
+    dom = max(stage_ms, key=stage_ms.get)
+    dom_op = next(op for op in ops if dom.startswith(op.w.name + ":"))
+    kname = dom.split(":")[1]
+    elem = 2
+    per_token = {"causal_chunk": 4 * dom_op.w.d * elem,   # q, k, v read + out written
+                 "bidir_out": 2 * dom_op.w.d * elem,      # q read + out written
+                 "kv_partial": 2 * dom_op.w.d * elem}.get(kname, 0)
+    alg_bytes = per_token * dom_op.w.tokens
+    dom_s = stage_ms[dom] * 1e-3
+    achieved = alg_bytes / dom_s / 1e9 if dom_s > 0 else 0.0
+    src_hash = kernel_source_hash()
+
+    result = {
+        "metric": "FAVOR+ tokens/s (B*H*L/s), bidir L=4096 + causal L=8192, one step each",
+        "value": tokens_per_step / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian Q/K/V, seeded orthogonal projection)",
+        "config": {"workload": "bidir B4 H8 L4096 d64 m256 (shared omega) + causal B2 H8 L8192 d64 m256 (omega per head)",
+                   "tokens_per_step": tokens_per_step, "chunk": 32},
+        "roofline": {"bound": "hbm", "kernel": kname, "op": dom_op.w.name, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_for(kname, src_hash), "alg_bytes_per_launch": alg_bytes,
+                     "avg_launch_ms": stage_ms[dom]},
+        "per_op_tokens_per_s": {name: WORKLOADS[name].tokens / (ms * 1e-3) for name, ms in op_ms.items()},
+        "stage_ms": stage_ms,
+        "wall_s_timed_region": wall,
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(ops)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -110,6 +110,23 @@ favor_status favor_causal(const favor_shape *shape, const void *q, const void *k
                           void *stream);
 
 /*
+ * Stage-timed variants.  Identical results to favor_bidir / favor_causal;
+ * additionally, events[i] (caller-created hipEvent_t handles) is recorded on
+ * `stream` before stage i and events[FAVOR_N_STAGES] after the last stage.
+ * Stages: 0 projection packing, 1 segment partials of phi(K)^T [V | 1],
+ * 2 merge over segments (bidir) / exclusive scan (causal), 3 output pass
+ * (bidir) / chunked scan (causal).  n_events must be >= FAVOR_N_STAGES + 1,
+ * else FAVOR_ERR_INVALID_ARG.  For callers measuring each kernel.
+ */
+#define FAVOR_N_STAGES 4
+favor_status favor_bidir_profiled(const favor_shape *shape, const void *q, const void *k, const void *v,
+                                  const float *omega, void *out, void *ws, size_t ws_bytes, void *stream,
+                                  void *const *events, int n_events);
+favor_status favor_causal_profiled(const favor_shape *shape, const void *q, const void *k, const void *v,
+                                   const float *omega, void *out, int chunk, void *ws, size_t ws_bytes,
+                                   void *stream, void *const *events, int n_events);
+
+/*
  * Seeded orthogonal random projection, written to HOST memory
  * omega_host[n_heads, m, d] (fp32), computed on the CPU.  For each head,
  * ceil(m/d) independent blocks: a d x d Gaussian whose rows are

@@ -12,6 +12,7 @@ FAVOR_BF16 = 1
 FAVOR_OP_FEATURES = 0
 FAVOR_OP_BIDIR = 1
 FAVOR_OP_CAUSAL = 2
+FAVOR_N_STAGES = 4
 
 STATUS = {0: "FAVOR_OK", 1: "FAVOR_ERR_INVALID_ARG", 2: "FAVOR_ERR_UNSUPPORTED", 3: "FAVOR_ERR_WORKSPACE",
           4: "FAVOR_ERR_HIP"}
@@ -55,6 +56,11 @@ def load() -> ctypes.CDLL:
     lib.favor_bidir.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.favor_causal.restype = ctypes.c_int
     lib.favor_causal.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    for name, chunk in (("favor_bidir_profiled", False), ("favor_causal_profiled", True)):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [sp, vp, vp, vp, vp, vp] + ([ctypes.c_int] if chunk else []) + [vp, sz, vp,
+                                                                                       ctypes.POINTER(vp), ctypes.c_int]
     lib.favor_orf_omega.restype = ctypes.c_int
     lib.favor_orf_omega.argtypes = [ctypes.c_ulonglong, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.favor_status_string.restype = ctypes.c_char_p

@@ -80,7 +80,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 favor_status run(int op, const favor_shape* s, const void* q, const void* k, const void* v, const float* omega,
-                 void* out, float* phi, float* log_scale, int stabilize, void* ws, size_t ws_bytes, void* stream) {
+                 void* out, float* phi, float* log_scale, int stabilize, void* ws, size_t ws_bytes, void* stream,
+                 void* const* events = nullptr) {
     favor_status st = check_shape(s, op);
     if (st != FAVOR_OK) return st;
     if (s->L == 0) return FAVOR_OK;
@@ -122,6 +123,7 @@ favor_status run(int op, const favor_shape* s, const void* q, const void* k, con
     a.ws_carry = reinterpret_cast<float*>(base + off); off += p.carry;
     a.ws_cmax = reinterpret_cast<float*>(base + off); off += p.cmax;
     a.stream = static_cast<hipStream_t>(stream);
+    a.events = events;
     return favor::launch(a) == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
@@ -151,6 +153,25 @@ favor_status favor_causal(const favor_shape* shape, const void* q, const void* k
                           void* out, int chunk, void* ws, size_t ws_bytes, void* stream) {
     if (chunk != 0 && chunk != 32) return FAVOR_ERR_UNSUPPORTED;
     return run(FAVOR_OP_CAUSAL, shape, q, k, v, omega, out, nullptr, nullptr, 0, ws, ws_bytes, stream);
+}
+
+favor_status favor_bidir_profiled(const favor_shape* shape, const void* q, const void* k, const void* v,
+                                  const float* omega, void* out, void* ws, size_t ws_bytes, void* stream,
+                                  void* const* events, int n_events) {
+    if (!events || n_events < FAVOR_N_STAGES + 1) return FAVOR_ERR_INVALID_ARG;
+    for (int i = 0; i <= FAVOR_N_STAGES; ++i)
+        if (!events[i]) return FAVOR_ERR_INVALID_ARG;
+    return run(FAVOR_OP_BIDIR, shape, q, k, v, omega, out, nullptr, nullptr, 0, ws, ws_bytes, stream, events);
+}
+
+favor_status favor_causal_profiled(const favor_shape* shape, const void* q, const void* k, const void* v,
+                                   const float* omega, void* out, int chunk, void* ws, size_t ws_bytes, void* stream,
+                                   void* const* events, int n_events) {
+    if (!events || n_events < FAVOR_N_STAGES + 1) return FAVOR_ERR_INVALID_ARG;
+    for (int i = 0; i <= FAVOR_N_STAGES; ++i)
+        if (!events[i]) return FAVOR_ERR_INVALID_ARG;
+    if (chunk != 0 && chunk != 32) return FAVOR_ERR_UNSUPPORTED;
+    return run(FAVOR_OP_CAUSAL, shape, q, k, v, omega, out, nullptr, nullptr, 0, ws, ws_bytes, stream, events);
 }
 
 const char* favor_status_string(favor_status status) {

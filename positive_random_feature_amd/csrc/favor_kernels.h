@@ -32,6 +32,9 @@ struct LaunchArgs {
     float* ws_carry;
     float* ws_cmax;
     hipStream_t stream;
+    // optional stage events: events[i] before stage i, events[n_stages] after
+    // the last one (nullptr: none)
+    void* const* events;
 };
 
 struct CausalCfg {

@@ -794,6 +794,10 @@ __global__ __launch_bounds__(256) void features_kernel(const T* __restrict__ x, 
 // ---------------------------------------------------------------------------
 // Host-side launchers (internal interface, see favor_kernels.h).
 // ---------------------------------------------------------------------------
+static inline void stage_event(const LaunchArgs& a, int i) {
+    if (a.events) (void)hipEventRecord(static_cast<hipEvent_t>(a.events[i]), a.stream);
+}
+
 template <typename T, int D, int FW, int MAXW>
 static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long long om_head_vecs, const T* q,
                                 const T* k, const T* v, T* out) {
@@ -803,6 +807,7 @@ static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H), dim3(64 * W), smem, a.stream, q, k, v, ompack, om_head_vecs,
                        a.ws_carry, a.ws_cmax, out, a.H, a.L, a.m, a.seg_len, a.nseg);
+    stage_event(a, 4);
     return hipGetLastError();
 }
 
@@ -813,11 +818,13 @@ static hipError_t launch_all(const LaunchArgs& a) {
     const int om_heads = a.omega_per_head ? a.H : 1;
     vec8<T>* ompack = reinterpret_cast<vec8<T>*>(a.ws_ompack);
     hipStream_t st = a.stream;
+    stage_event(a, 0);
     {
         const long long total = (long long)om_heads * (a.m / 16) * KSD * 64;
         const int blocks = (int)std::min<long long>((total + 255) / 256, 4096);
         hipLaunchKernelGGL((pack_omega_kernel<T, D>), dim3(blocks), dim3(256), 0, st, a.omega, ompack, om_heads, a.m);
     }
+    stage_event(a, 1);
     const int BH = a.B * a.H;
     const T* q = reinterpret_cast<const T*>(a.q);
     const T* k = reinterpret_cast<const T*>(a.k);
@@ -834,10 +841,12 @@ static hipError_t launch_all(const LaunchArgs& a) {
     const int wpg = std::min(a.m, 256) / 32;  // waves per feature group
     hipLaunchKernelGGL((kv_partial_kernel<T, D>), dim3(a.nseg, BH, nfg), dim3(64 * wpg), 0, st, k, v, ompack,
                        om_head_vecs, a.ws_partial, a.ws_pmax, a.H, a.L, a.m, a.seg_len, a.nseg);
+    stage_event(a, 2);
     if (a.op == OpKind::Bidir) {
         hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(a.m / 32, BH), dim3(256), 0, st, a.ws_partial, a.ws_pmax,
                            a.m, a.nseg, a.nseg, 0, reinterpret_cast<vec8<T>*>(a.ws_kvpack), a.ws_mmax, nullptr,
                            nullptr, 0);
+        stage_event(a, 3);
         const int waves = 8;
         const int tok_per_wg = waves * 16 * (D >= 128 ? 2 : 4);
         const int blocks = (a.L + tok_per_wg - 1) / tok_per_wg;
@@ -859,9 +868,11 @@ static hipError_t launch_all(const LaunchArgs& a) {
             hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * waves), 0, st, q, ompack, om_head_vecs, kvp,
                                a.ws_mmax, out, a.H, a.L, a.m);
         }
+        stage_event(a, 4);
     } else {
         hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(a.m / 32, BH), dim3(256), 0, st, a.ws_partial, a.ws_pmax,
                            a.m, a.nseg, a.nseg, 1, nullptr, nullptr, a.ws_carry, a.ws_cmax, a.nseg);
+        stage_event(a, 3);
         const CausalCfg cfg = causal_config(D, a.m);
         if (cfg.fw == 32) return launch_causal<T, D, 32, 8>(a, ompack, om_head_vecs, q, k, v, out);
         if constexpr (D <= 64) {
