@@ -30,8 +30,8 @@ from positive_random_feature_amd import _lib  # noqa: E402
 from positive_random_feature_amd.workloads import WORKLOADS, make_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-STAGES = {"bidir": ["pack_omega", "kv_partial", "merge", "bidir_out"],
-          "causal": ["pack_omega", "kv_partial", "scan", "causal_chunk"]}
+STAGES = {"bidir": ["kv_partial", "merge", "bidir_out"],
+          "causal": ["kv_partial", "scan", "causal_chunk"]}
 KERNEL_SOURCES = ["positive_random_feature_amd/csrc/favor_kernels.hip", "positive_random_feature_amd/csrc/favor_device.h"]
 
 

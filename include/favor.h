@@ -27,8 +27,10 @@
  *   - Accumulation is fp32.  bf16 inputs give bf16 outputs.  There is no
  *     temperature: the library computes exp(q.k) exactly as defined; callers
  *     wanting softmax(q.k / sqrt(d)) pre-scale q and k by d^-1/4.
- *   - Supported: d in {16, 32, 64, 128}; m a multiple of 32, 32 <= m <= 512;
- *     B, H >= 1; L >= 0 (L = 0 is a no-op); B*H*L*d < 2^31.
+ *   - Supported: d in {16, 32, 64, 128}; m a multiple of 32, 32 <= m <= 512
+ *     (bidirectional and features), m in {32, 64, 128, 256, 512} (causal);
+ *     fp32 only with d <= 64; B, H >= 1; L >= 0 (L = 0 is a no-op);
+ *     B*H*L*d < 2^31.
  */
 #ifndef FAVOR_H_
 #define FAVOR_H_
@@ -113,12 +115,13 @@ favor_status favor_causal(const favor_shape *shape, const void *q, const void *k
  * Stage-timed variants.  Identical results to favor_bidir / favor_causal;
  * additionally, events[i] (caller-created hipEvent_t handles) is recorded on
  * `stream` before stage i and events[FAVOR_N_STAGES] after the last stage.
- * Stages: 0 projection packing, 1 segment partials of phi(K)^T [V | 1],
- * 2 merge over segments (bidir) / exclusive scan (causal), 3 output pass
- * (bidir) / chunked scan (causal).  n_events must be >= FAVOR_N_STAGES + 1,
- * else FAVOR_ERR_INVALID_ARG.  For callers measuring each kernel.
+ * Stages: 0 segment partials of phi(K)^T [V | 1], 1 merge over segments
+ * (bidir) / exclusive scan (causal), both also packing the projection,
+ * 2 output pass (bidir) / chunked scan (causal).  n_events must be
+ * >= FAVOR_N_STAGES + 1, else FAVOR_ERR_INVALID_ARG.  For callers measuring
+ * each kernel.
  */
-#define FAVOR_N_STAGES 4
+#define FAVOR_N_STAGES 3
 favor_status favor_bidir_profiled(const favor_shape *shape, const void *q, const void *k, const void *v,
                                   const float *omega, void *out, void *ws, size_t ws_bytes, void *stream,
                                   void *const *events, int n_events);

@@ -12,7 +12,7 @@ FAVOR_BF16 = 1
 FAVOR_OP_FEATURES = 0
 FAVOR_OP_BIDIR = 1
 FAVOR_OP_CAUSAL = 2
-FAVOR_N_STAGES = 4
+FAVOR_N_STAGES = 3
 
 STATUS = {0: "FAVOR_OK", 1: "FAVOR_ERR_INVALID_ARG", 2: "FAVOR_ERR_UNSUPPORTED", 3: "FAVOR_ERR_WORKSPACE",
           4: "FAVOR_ERR_HIP"}

@@ -28,6 +28,7 @@ favor_status check_shape(const favor_shape* s, int op) {
     if (s->d != 16 && s->d != 32 && s->d != 64 && s->d != 128) return FAVOR_ERR_UNSUPPORTED;
     if (s->m % 32 != 0 || s->m > 512) return FAVOR_ERR_UNSUPPORTED;
     if (s->m > 256 && s->m % 64 != 0) return FAVOR_ERR_UNSUPPORTED;
+    if (s->dtype == FAVOR_F32 && s->d > 64) return FAVOR_ERR_UNSUPPORTED;
     if (s->omega_head_stride != 0 && s->omega_head_stride != (long long)s->m * s->d) return FAVOR_ERR_INVALID_ARG;
     const long long elems = (long long)s->B * s->H * s->L * s->d;
     if (elems >= (1LL << 31)) return FAVOR_ERR_UNSUPPORTED;

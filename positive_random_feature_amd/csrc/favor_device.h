@@ -88,6 +88,18 @@ __device__ __forceinline__ f8 load8(const float* p) {
     return f8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
 
+// The same loads through an explicitly global pointer: when a pointer's
+// address space cannot be inferred (e.g. picked from an array at run time)
+// the compiler emits flat loads, which also count against the LDS wait
+// counter and so serialise with every later LDS access.
+typedef __attribute__((address_space(1))) const bf16x8 gbf16x8;
+typedef __attribute__((address_space(1))) const f4 gf4;
+__device__ __forceinline__ bf16x8 gload8(const bf16* p) { return *(gbf16x8*)(p); }
+__device__ __forceinline__ f8 gload8(const float* p) {
+    const f4 a = ((gf4*)(p))[0], b = ((gf4*)(p))[1];
+    return f8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 // Lane exchanges (ds_bpermute through __shfl_xor).
 // Sum / max over the four lanes r, r+16, r+32, r+48 (the lanes holding one
 // token column in B-operand layout).
@@ -100,6 +112,42 @@ __device__ __forceinline__ float col_max(float x) {
     return __builtin_fmaxf(x, __shfl_xor(x, 32));
 }
 
+// DPP lane permutations inside rows of 16 lanes (no LDS traffic).
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within 16 lanes
+
+// Sum over N consecutive lanes (N = 2, 4, 8, 16; groups aligned to N); every
+// lane of a group gets the group's sum.
+template <int N> __device__ __forceinline__ float group_sum(float x) {
+    if (N >= 2) x += dpp<kDppXor1>(x);
+    if (N >= 4) x += dpp<kDppXor2>(x);
+    if (N >= 8) x += dpp<kDppHalfMirror>(x);
+    if (N >= 16) x += dpp<kDppMirror>(x);
+    return x;
+}
+
+// Max over the whole wave, uniform result (rows reduced with DPP, then the
+// four row results combined through scalar reads).
+__device__ __forceinline__ float wave_max_uniform(float x) {
+    x = __builtin_fmaxf(x, dpp<kDppXor1>(x));
+    x = __builtin_fmaxf(x, dpp<kDppXor2>(x));
+    x = __builtin_fmaxf(x, dpp<kDppHalfMirror>(x));
+    x = __builtin_fmaxf(x, dpp<kDppMirror>(x));
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) x = __builtin_fmaxf(x, __shfl_xor(x, o));
@@ -107,6 +155,56 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane s supplies the address of a 4-element chunk M[s][0..3]; lane i
+// receives {M[4j + i/4][i % 4] : j = 0..3}.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// Row-major LDS tile of 32 rows; rows padded by 16 bytes so that 16 lanes
+// reading 16-byte pieces of 16 consecutive rows hit distinct banks.
+template <typename T, int COLS> struct LdsTile {
+    static constexpr int RS = COLS + 16 / (int)sizeof(T);  // row stride, elements
+    static constexpr int ELEMS = 32 * RS;
+};
+
+// Operand holding, for column `col` (= col0 + r), the 8 rows in kappa order
+// {4g..4g+3, 16+4g..16+4g+3} of a row-major 32-row LDS tile: the B operand of
+// a contraction over the tile's rows.  bf16: two transpose reads (lane
+// (q, s = 4j + c) points at row 4q + j, columns col0 + 4c..+3).
+template <int RS>
+__device__ __forceinline__ bf16x8 kappa_col(const bf16* tile, int col0, int lane) {
+    const int q = lane >> 4, s = lane & 15;
+    const bf16* p0 = tile + (4 * q + (s >> 2)) * RS + col0 + 4 * (s & 3);
+    const bf16x4 lo = lds_read_tr16(p0);
+    const bf16x4 hi = lds_read_tr16(p0 + 16 * RS);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <int RS>
+__device__ __forceinline__ f8 kappa_col(const float* tile, int col0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const float* p = tile + col0 + r;
+    f8 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = p[(4 * g + i) * RS];
+        v[4 + i] = p[(16 + 4 * g + i) * RS];
+    }
+    return v;
+}
+
+// Store 4 consecutive elements (one D-tile column quad) into LDS.
+__device__ __forceinline__ void lds_store4(bf16* p, f4 v) {
+    bf16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x4*>(p) = r;
+}
+__device__ __forceinline__ void lds_store4(float* p, f4 v) { *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]}; }
 
 // Store 4 consecutive output elements.
 __device__ __forceinline__ void store4(bf16* p, f4 v) {

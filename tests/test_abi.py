@@ -96,6 +96,9 @@ def test_validation(lib, fn):
 def test_causal_chunk_and_lds_limits(lib):
     assert _causal(lib, shp(), chunk=64) == UNSUPPORTED
     assert _causal(lib, shp(), chunk=-1) == UNSUPPORTED
+    assert _causal(lib, shp(m=96)) == UNSUPPORTED      # causal: m in {32, 64, 128, 256, 512}
+    assert _bidir(lib, shp(m=96), nbytes=1 << 40) != UNSUPPORTED
+    assert _bidir(lib, shp(d=128, dtype=_lib.FAVOR_F32)) == UNSUPPORTED
     # fp32 d=128 m=512: the causal state does not fit one workgroup's LDS
     assert _causal(lib, shp(d=128, m=512, dtype=_lib.FAVOR_F32)) == UNSUPPORTED
 
