@@ -56,7 +56,9 @@ Plan make_plan(int op, const favor_shape& s) {
     if (nseg < 1) nseg = 1;
     if (nseg > tiles) nseg = tiles;
     const int per = (s.L + nseg - 1) / nseg;
-    p.seg_len = ((per + 31) / 32) * 32;
+    // causal segments are whole 64-token chunks where possible
+    const int gran = op == FAVOR_OP_CAUSAL && s.L >= 64 * nseg ? 64 : 32;
+    p.seg_len = ((per + gran - 1) / gran) * gran;
     p.nseg = (s.L + p.seg_len - 1) / p.seg_len;
     const size_t rows = (size_t)BH * p.nseg * m;
     p.partial = align256(rows * (D + 1) * sizeof(float));

@@ -100,6 +100,10 @@ __device__ __forceinline__ f8 gload8(const float* p) {
     return f8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+template <typename V> __device__ __forceinline__ V gload_vec(const V* p) {
+    return *(__attribute__((address_space(1))) const V*)(p);
+}
+
 // Lane exchanges (ds_bpermute through __shfl_xor).
 // Sum / max over the four lanes r, r+16, r+32, r+48 (the lanes holding one
 // token column in B-operand layout).

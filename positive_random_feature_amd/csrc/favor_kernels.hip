@@ -32,6 +32,7 @@
 #include "favor_kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace favor {
 
@@ -67,6 +68,40 @@ __global__ __launch_bounds__(256) void pack_omega_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Swizzled LDS layouts (bank-conflict free for row reads, 16-lane row-chunk
+// reads and transpose reads alike; the row strides are 8 words mod 32).
+// 64-column bf16 tile: the 16-byte chunk c of row r sits at chunk c ^ ((r >> 2) & 1).
+constexpr int kSwzTileRS = 80;
+__device__ __forceinline__ int swz_tile(int row, int col) {
+    return row * kSwzTileRS + (((col >> 3) ^ ((row >> 2) & 1)) << 3) + (col & 7);
+}
+// Row-major bf16 array of row stride RS: the 8-byte chunk c of row r sits at
+// chunk c ^ ((r >> 2) & 3).
+template <int RS>
+__device__ __forceinline__ int swz_rows(int row, int col) {
+    return row * RS + (((col >> 2) ^ ((row >> 2) & 3)) << 2) + (col & 3);
+}
+// Both swizzles only permute chunks inside aligned 16-column groups and
+// depend on row bits 2..3, so for row0 and col0 multiples of 16,
+// off(row0 + r, col0 + c) = off(r, c) + row0 * RS + col0: a lane offset plus
+// a constant (an immediate in the LDS instruction).
+//
+// kappa_col (rows {4g..4g+3, 16+4g..16+4g+3} of column r) in a swizzled array:
+// p = base + lane offset + row0 * RS + col0, with the lane offset from
+// kappa_lane_off(); the second read is 16 rows further.
+template <typename Off>
+__device__ __forceinline__ int kappa_lane_off(int lane, Off off) {
+    const int q = lane >> 4, s = lane & 15;
+    return off(4 * q + (s >> 2), 4 * (s & 3));
+}
+template <int RS>
+__device__ __forceinline__ bf16x8 kappa_col_at(const bf16* p) {
+    const bf16x4 lo = lds_read_tr16(p);
+    const bf16x4 hi = lds_read_tr16(p + 16 * RS);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---------------------------------------------------------------------------
 // Tile prefetch: NTEN tensors, each a 32-row tile of D columns, split into
 // 8-element chunks (chunk c of a tensor = row c / (D/8), columns 8 (c % (D/8))).
 // load() issues global loads into registers; store() writes them to LDS
@@ -85,26 +120,48 @@ struct Prefetch {
     // Branch-free (so the compiler can count the loads in flight): rows are
     // clamped to t_max, a valid row of every tensor; rows at or past t_end
     // are replaced by zeros when stored.
+    // chunk index of load i: tensor and position in it (compile-time tensor
+    // when every tensor is a whole number of thread blocks)
+    __device__ __forceinline__ static void where(int i, int& tn, int& cc) {
+        if constexpr (CH % NTHR == 0) {
+            tn = (i * NTHR) / CH;
+            cc = (i * NTHR) % CH + (int)threadIdx.x;
+        } else {
+            int c = threadIdx.x + i * NTHR;
+            if (TOT % NTHR != 0) c = min(c, TOT - 1);
+            tn = c / CH;
+            cc = c % CH;
+        }
+    }
     __device__ __forceinline__ void load(const T* const* src, int t0, int t_max) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            int c = threadIdx.x + i * NTHR;
-            if (TOT % NTHR != 0) c = min(c, TOT - 1);
-            const int tn = c / CH, cc = c % CH;
+            int tn, cc;
+            where(i, tn, cc);
             const int t = min(t0 + cc / CPR, t_max);
             v[i] = gload8(src[tn] + (size_t)t * D + 8 * (cc % CPR));
         }
     }
+    // SWZ: the destination tiles use swz_tile (bf16, D = 64)
+    template <bool SWZ = false>
     __device__ __forceinline__ void store(T* const* dst, float* nrm, int norm_mask, int t0, int t_end) const {
         constexpr int RS = LdsTile<T, D>::RS;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int c = threadIdx.x + i * NTHR;
             if (TOT % NTHR == 0 || c < TOT) {
-                const int tn = c / CH, cc = c % CH;
+                int tn, cc;
+                where(i, tn, cc);
                 const int row = cc / CPR, col = 8 * (cc % CPR);
                 const vec8<T> x = (t0 + row < t_end) ? v[i] : zero8<T>();
-                *reinterpret_cast<vec8<T>*>(dst[tn] + row * RS + col) = x;
+                // a select over constant indices (not dst[tn]) keeps the LDS
+                // address space visible to the compiler: no flat stores
+                T* d = dst[0];
+#pragma unroll
+                for (int u = 1; u < NTEN; ++u) d = (tn == u) ? dst[u] : d;
+                int off = row * RS + col;
+                if constexpr (SWZ) off = swz_tile(row, col);
+                *reinterpret_cast<vec8<T>*>(d + off) = x;
                 if ((norm_mask >> tn) & 1) {
                     float ss = 0.0f;
 #pragma unroll
@@ -706,7 +763,7 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
                 if (!OM_REGS) asm volatile("" : "+s"(omc));
                 auto om_op = [&](int ft, int ks) -> vec8<T> {
                     if (OM_REGS) return omr[OM_REGS ? ft : 0][OM_REGS ? ks : 0];
-                    return omc[((size_t)(f0 / 16 + ft) * KSD + ks) * 64 + lane];
+                    return gload_vec(omc + ((size_t)(f0 / 16 + ft) * KSD + ks) * 64 + lane);
                 };
 
                 // ---- queries: projection, per-token shift over this wave's features
@@ -834,6 +891,291 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
 }
 
 // ---------------------------------------------------------------------------
+// causal_tile: chunked causal scan for bf16, d = 64, m <= 256.  One workgroup
+// of four waves per (segment, head); chunks of 64 tokens.  Wave w has two
+// roles in every chunk:
+//   token role   tokens 16w..16w+15 of the chunk: the query and key
+//                projections over all m features (so the per-query shift is
+//                a wave-local maximum), phi(Q) and phi(K) published in LDS,
+//                then the intra-chunk scores S^T[key][query] for keys <= query
+//                and S [V | 1] for its 16 queries;
+//   column role  value columns 16w..16w+15: the state slice G[:, cols]
+//                (all m features, fp32 registers), the inter-chunk term
+//                phi(Q) G for all 64 queries (published in LDS) and the state
+//                update G += phi(K)^T V; also z = sum phi(k) for the feature
+//                blocks kb = w (mod 4), which gives partial denominators.
+// All keys of a segment share one shift (the largest carry-in block shift)
+// and each query one shift over all features, so the contraction over
+// features is exact up to factors that cancel in the ratio (Simple
+// Derivation).  Two barriers per chunk: phi published, then the next chunk's
+// tiles and this chunk's inter-chunk terms published; outputs of a chunk are
+// written at the start of the next step.
+// ---------------------------------------------------------------------------
+template <int M>
+struct TileSmem {
+    static constexpr int D = 64, KSD = 2, NFB = M / 32, NFT = M / 16;
+    static constexpr int RS = kSwzTileRS;           // Q/K/V tile row stride (swz_tile)
+    static constexpr int PKS = M + 16;               // phi(K) row stride (bf16, swz_rows)
+    static constexpr int OS = D + 4;                 // inter-chunk output row stride (fp32)
+    static constexpr size_t TILE = (size_t)64 * RS;  // elements of a 64-row tile
+    static constexpr size_t OFF_OM = 0;
+    static constexpr size_t OFF_TQ = OFF_OM + sizeof(bf16x8) * (size_t)NFT * KSD * 64;
+    static constexpr size_t OFF_TK = OFF_TQ + sizeof(bf16) * TILE;
+    static constexpr size_t OFF_TV = OFF_TK + sizeof(bf16) * TILE;
+    static constexpr size_t OFF_NRM = OFF_TV + sizeof(bf16) * 2 * TILE;
+    static constexpr size_t OFF_PQ = OFF_NRM + sizeof(float) * 128;
+    static constexpr size_t OFF_PK = OFF_PQ + sizeof(bf16x8) * (size_t)4 * NFB * 64;
+    static constexpr size_t OFF_OI = OFF_PK + sizeof(bf16) * (size_t)64 * PKS;
+    static constexpr size_t OFF_DP = OFF_OI + sizeof(float) * (size_t)64 * OS;
+    static constexpr size_t BYTES = OFF_DP + sizeof(float) * 4 * 64;
+};
+
+template <int M>
+// At most 256 registers: the state stays in VGPRs (no accumulator-register copies).
+__global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                          const bf16* __restrict__ v, const bf16x8* __restrict__ ompack,
+                                                          long long om_head_vecs, const float* __restrict__ carry,
+                                                          const float* __restrict__ cmax, bf16* __restrict__ out, int H,
+                                                          int L, int seg_len, int nseg) {
+    using SM = TileSmem<M>;
+    constexpr int D = SM::D, KSD = SM::KSD, NFB = SM::NFB, NFT = SM::NFT, RS = SM::RS, PKS = SM::PKS, OS = SM::OS;
+    constexpr int D1 = D + 1;
+    constexpr int ZB = (NFB + 3) / 4;  // z blocks per wave (kb = w + 4 zb)
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    bf16x8* om = reinterpret_cast<bf16x8*>(smem_raw + SM::OFF_OM);
+    bf16* tq = reinterpret_cast<bf16*>(smem_raw + SM::OFF_TQ);
+    bf16* tk = reinterpret_cast<bf16*>(smem_raw + SM::OFF_TK);
+    bf16* tv0 = reinterpret_cast<bf16*>(smem_raw + SM::OFF_TV);
+    float* nrm = reinterpret_cast<float*>(smem_raw + SM::OFF_NRM);  // [half][K rows | Q rows]
+    bf16x8* phq = reinterpret_cast<bf16x8*>(smem_raw + SM::OFF_PQ);
+    bf16* phk = reinterpret_cast<bf16*>(smem_raw + SM::OFF_PK);
+    float* oin = reinterpret_cast<float*>(smem_raw + SM::OFF_OI);
+    float* dpart = reinterpret_cast<float*>(smem_raw + SM::OFF_DP);
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
+    const int seg = blockIdx.x, bh = blockIdx.y, h = bh % H;
+    const int t_begin = seg * seg_len;
+    const int t_end = min(L, t_begin + seg_len);
+    const int nch = (t_end - t_begin + 63) / 64;
+    const size_t xbase = (size_t)bh * L * D;
+    const bf16* src[3] = {k + xbase, q + xbase, v + xbase};
+
+    // chunk 0 into registers
+    Prefetch<bf16, D, 256, 3> pf[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) pf[hf].load(src, t_begin + 32 * hf, L - 1);
+
+    // projection operands of this head into LDS
+    {
+        const bf16x8* omh = ompack + (size_t)(om_head_vecs ? h : 0) * (size_t)om_head_vecs;
+        for (int e = threadIdx.x; e < NFT * KSD * 64; e += 256) om[e] = omh[e];
+    }
+
+    // carry-in: state slice for columns 16w.. and z for this wave's blocks,
+    // rescaled from the per-block shifts to the segment's common key shift
+    const float* cm = cmax + ((size_t)bh * nseg + seg) * NFB;
+    float Mseg = kNegInf;
+#pragma unroll
+    for (int b = 0; b < NFB; ++b) Mseg = __builtin_fmaxf(Mseg, cm[b]);
+    f4 G[NFT];
+    f4 Z[2 * ZB];
+    {
+        const float* cb = carry + ((size_t)bh * nseg + seg) * (size_t)M * D1;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+            const float mb = cm[ft / 2];
+            const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G[ft][i] = sc * cb[(size_t)(16 * ft + 4 * g + i) * D1 + 16 * w + r];
+        }
+#pragma unroll
+        for (int zb = 0; zb < ZB; ++zb) {
+            const int kb = w + 4 * zb;
+            const bool own = kb < NFB;
+            const float mb = own ? cm[kb] : kNegInf;
+            const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Z[2 * zb + hf][i] = own ? sc * cb[(size_t)(32 * kb + 16 * hf + 4 * g + i) * D1 + D] : 0.0f;
+        }
+    }
+
+    auto stage_chunk = [&](int ci) {
+        // past the last chunk: rows of the last chunk, zeroed, into the V
+        // buffer the last chunk does not use
+        const int cc = min(ci, nch - 1);
+        bf16* tv = tv0 + (size_t)(ci & 1) * SM::TILE;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            bf16* dst[3] = {tk + 32 * hf * RS, tq + 32 * hf * RS, tv + 32 * hf * RS};
+            pf[hf].template store<true>(dst, nrm + 64 * hf, 3, t_begin + 64 * cc + 32 * hf, ci < nch ? t_end : -1);
+        }
+    };
+    auto prefetch_chunk = [&](int ci) {
+        const int cc = min(ci, nch - 1);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) pf[hf].load(src, t_begin + 64 * cc + 32 * hf, L - 1);
+    };
+
+    stage_chunk(0);
+    prefetch_chunk(1);
+    __syncthreads();
+
+    const bf16x8 ones = splat8<bf16>(1.0f);
+    f4 oi[5];  // intra-chunk terms of this wave's 16 queries: 4 column tiles, denominator
+    // lane offsets into the swizzled arrays (everything else is a constant)
+    const int off_trv = kappa_lane_off(lane, swz_tile);       // V, transpose reads
+    const int off_trk = kappa_lane_off(lane, swz_rows<PKS>);  // phi(K), transpose reads
+    const int off_row = swz_tile(r, 8 * g);                   // Q/K rows 16w + r
+    const int off_krow = swz_rows<PKS>(r, 4 * g);             // phi(K) rows 16 kt + r
+
+    // outputs of chunk cc for tokens 16w..16w+15
+    auto finalize = [&](int cc) {
+        const int row = 16 * w + r;
+        const int t = t_begin + 64 * cc + row;
+        float den = oi[4][0];
+#pragma unroll
+        for (int c = 0; c < (NFB < 4 ? NFB : 4); ++c) den += dpart[c * 64 + row];
+        const float inv = __builtin_amdgcn_rcpf(den);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const f4 o = *reinterpret_cast<const f4*>(oin + row * OS + 16 * ct + 4 * g) + oi[ct];
+            if (t < t_end) store4(out + xbase + (size_t)t * D + 16 * ct + 4 * g, o * inv);
+        }
+    };
+
+    for (int c = 0; c < nch; ++c) {
+        const int t0 = t_begin + 64 * c;
+        const bf16* tv = tv0 + (size_t)(c & 1) * SM::TILE;
+        if (c > 0) finalize(c - 1);
+
+        // ---- token role: projections of tokens 16w..16w+15
+        bf16x8 bq[NFB];
+        {
+            const int row = 16 * w + r;
+            const float* nh = nrm + 64 * (row >> 5);
+            const float ck = (t0 + row < t_end) ? nh[row & 31] - Mseg : kNegInf;
+            const float cq = nh[32 + (row & 31)];
+            bf16x8 xk[KSD], xq[KSD];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                xk[ks] = *reinterpret_cast<const bf16x8*>(tk + off_row + 16 * w * RS + 32 * ks);
+                xq[ks] = *reinterpret_cast<const bf16x8*>(tq + off_row + 16 * w * RS + 32 * ks);
+            }
+            f4 pq[NFT];
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) {
+                f4 pk = f4splat(ck);
+                pq[ft] = f4splat(cq);
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) {
+                    const bf16x8 a = om[(ft * KSD + ks) * 64 + lane];
+                    pk = mma32(a, xk[ks], pk);
+                    pq[ft] = mma32(a, xq[ks], pq[ft]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk[i] = exp2f_fast(pk[i]);
+                lds_store4(phk + off_krow + 16 * w * PKS + 16 * ft, pk);
+            }
+            float mx = kNegInf;
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[ft][i]);
+            mx = col_max(mx);
+#pragma unroll
+            for (int kb = 0; kb < NFB; ++kb) {
+                f4 e0, e1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    e0[i] = exp2f_fast(pq[2 * kb][i] - mx);
+                    e1[i] = exp2f_fast(pq[2 * kb + 1][i] - mx);
+                }
+                bq[kb] = pack8t<bf16>(e0, e1);
+                phq[(w * NFB + kb) * 64 + lane] = bq[kb];
+            }
+        }
+        __syncthreads();
+
+        // next chunk's tiles (Q, K and this V buffer's partner are free now)
+        stage_chunk(c + 1);
+        prefetch_chunk(c + 2);
+
+        // ---- token role: intra-chunk terms for queries 16w..16w+15
+        {
+            // every wave runs the full 64 x 64 block (the last wave needs all
+            // of it, so this costs no time) and zeroes keys after the query
+            f4 st[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                st[kt] = f4splat(0.0f);
+                const bf16* pr = phk + off_krow + 16 * kt * PKS;
+#pragma unroll
+                for (int kb = 0; kb < NFB; ++kb) {
+                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(pr + 32 * kb);
+                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(pr + 32 * kb + 16);
+                    const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    st[kt] = mma32(a, bq[kb], st[kt]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * kt + 4 * g + i > 16 * w + r) st[kt][i] = 0.0f;
+            }
+#pragma unroll
+            for (int ct = 0; ct < 5; ++ct) oi[ct] = f4splat(0.0f);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8 b = pack8t<bf16>(st[2 * j], st[2 * j + 1]);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) oi[ct] = mma32(kappa_col_at<RS>(tv + off_trv + 32 * j * RS + 16 * ct), b, oi[ct]);
+                oi[4] = mma32(ones, b, oi[4]);
+            }
+        }
+
+        // ---- column role: inter-chunk terms phi(Q) G for all 64 queries
+        {
+            bf16x8 ga[NFB];
+#pragma unroll
+            for (int kb = 0; kb < NFB; ++kb) ga[kb] = pack8t<bf16>(G[2 * kb], G[2 * kb + 1]);
+            bf16x8 za[ZB];
+#pragma unroll
+            for (int zb = 0; zb < ZB; ++zb) za[zb] = pack8t<bf16>(Z[2 * zb], Z[2 * zb + 1]);
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt) {
+                f4 o = f4splat(0.0f);
+#pragma unroll
+                for (int kb = 0; kb < NFB; ++kb) o = mma32(ga[kb], phq[(qt * NFB + kb) * 64 + lane], o);
+                *reinterpret_cast<f4*>(oin + (16 * qt + r) * OS + 16 * w + 4 * g) = o;
+                // z blocks past m are zero (their index is clamped for the read)
+                f4 dz = f4splat(0.0f);
+#pragma unroll
+                for (int zb = 0; zb < ZB; ++zb)
+                    dz = mma32(za[zb], phq[(qt * NFB + min(w + 4 * zb, NFB - 1)) * 64 + lane], dz);
+                if (g == 0 && w < NFB) dpart[w * 64 + 16 * qt + r] = dz[0];
+            }
+        }
+
+        // ---- column role: state update G += phi(K)^T V, z += phi(K)^T 1
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const bf16* pj = phk + off_trk + 32 * j * PKS;
+            const bf16x8 bv = kappa_col_at<RS>(tv + off_trv + 32 * j * RS + 16 * w);
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) G[ft] = mma32(kappa_col_at<PKS>(pj + 16 * ft), bv, G[ft]);
+#pragma unroll
+            for (int zt = 0; zt < 2 * ZB; ++zt) {
+                const int ft = min(2 * (w + 4 * (zt / 2)) + (zt % 2), NFT - 1);
+                Z[zt] = mma32(kappa_col_at<PKS>(pj + 16 * ft), ones, Z[zt]);
+            }
+        }
+        __syncthreads();
+    }
+    finalize(nch - 1);
+}
+
+// ---------------------------------------------------------------------------
 // features: phi(x) (fp32) for 16 tokens per wave, all m features; optional
 // per-row stabiliser (two passes: the maximum, then the features).
 // ---------------------------------------------------------------------------
@@ -920,6 +1262,18 @@ static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long
     return hipGetLastError();
 }
 
+template <int M>
+static hipError_t launch_causal_tile(const LaunchArgs& a, const bf16x8* ompack, long long om_head_vecs, const bf16* q,
+                                     const bf16* k, const bf16* v, bf16* out) {
+    constexpr size_t bytes = TileSmem<M>::BYTES;
+    static_assert(bytes <= kMaxLds, "causal_tile LDS");
+    auto kern = causal_tile_kernel<M>;
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H), dim3(256), bytes, a.stream, q, k, v, ompack, om_head_vecs,
+                       a.ws_carry, a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t launch_all(const LaunchArgs& a) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
@@ -980,6 +1334,15 @@ static hipError_t launch_all(const LaunchArgs& a) {
         }
         stage_event(a, 3);
         return hipGetLastError();
+    }
+    if constexpr (std::is_same<T, bf16>::value && D == 64) {
+        if (a.m == 64 || a.m == 128 || a.m == 256) {
+            hipError_t err = a.m == 64    ? launch_causal_tile<64>(a, ompack, om_head_vecs, q, k, v, out)
+                             : a.m == 128 ? launch_causal_tile<128>(a, ompack, om_head_vecs, q, k, v, out)
+                                          : launch_causal_tile<256>(a, ompack, om_head_vecs, q, k, v, out);
+            stage_event(a, 3);
+            return err;
+        }
     }
     const CausalCfg cfg = causal_config(D, a.m);
     hipError_t err = hipErrorInvalidValue;

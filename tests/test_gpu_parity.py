@@ -181,7 +181,8 @@ def test_large_norm_stabilisers(op):
 @pytest.mark.parametrize("d,m,op", [(16, 32, "bidir"), (32, 64, "bidir"), (64, 96, "bidir"), (128, 128, "bidir"),
                                      (128, 256, "bidir"), (64, 512, "bidir"), (32, 160, "bidir"), (128, 512, "bidir"),
                                      (16, 32, "causal"), (32, 64, "causal"), (64, 128, "causal"), (128, 128, "causal"),
-                                     (128, 256, "causal"), (64, 512, "causal"), (16, 256, "causal"), (128, 64, "causal")])
+                                     (128, 256, "causal"), (64, 512, "causal"), (16, 256, "causal"), (128, 64, "causal"),
+                                     (64, 64, "causal")])
 def test_other_shapes(d, m, op):
     w = WORKLOADS["causal_bf16_8k"].replace(d=d, m=m)
     inp, om, got = _run(w, op, 1, 2, 333)
