@@ -50,14 +50,16 @@ Plan make_plan(int op, const favor_shape& s) {
         p.total = p.ompack;
         return p;
     }
-    const int nfg = (m + 255) / 256;
+    const int nfg = (m + 255) / 256;  // feature groups of the partial pass
+    // one partial-pass (bidirectional) or chunk-scan (causal) workgroup per
+    // compute unit
     int nseg = op == FAVOR_OP_BIDIR ? (kTargetWorkgroups + BH * nfg - 1) / (BH * nfg)
                                     : (kTargetWorkgroups + BH - 1) / BH;
     if (nseg < 1) nseg = 1;
     if (nseg > tiles) nseg = tiles;
     const int per = (s.L + nseg - 1) / nseg;
-    // causal segments are whole 64-token chunks where possible
-    const int gran = op == FAVOR_OP_CAUSAL && s.L >= 64 * nseg ? 64 : 32;
+    // segments are whole 64-token steps where possible
+    const int gran = s.L >= 64 * nseg ? 64 : 32;
     p.seg_len = ((per + gran - 1) / gran) * gran;
     p.nseg = (s.L + p.seg_len - 1) / p.seg_len;
     const size_t rows = (size_t)BH * p.nseg * m;

@@ -102,17 +102,17 @@ __device__ __forceinline__ bf16x8 kappa_col_at(const bf16* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile prefetch: NTEN tensors, each a 32-row tile of D columns, split into
+// Tile prefetch: NTEN tensors, each a ROWS-row tile of D columns, split into
 // 8-element chunks (chunk c of a tensor = row c / (D/8), columns 8 (c % (D/8))).
 // load() issues global loads into registers; store() writes them to LDS
 // tiles and, for the tensors in `norm_mask`, the row constants
 // -log2(e)|x|^2/2, each summed over the D/8 consecutive lanes that hold one
 // row (DPP, no LDS round trip).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NTHR, int NTEN>
+template <typename T, int D, int NTHR, int NTEN, int ROWS = 32>
 struct Prefetch {
     static constexpr int CPR = D / 8;
-    static constexpr int CH = 32 * CPR;
+    static constexpr int CH = ROWS * CPR;
     static constexpr int TOT = CH * NTEN;
     static constexpr int PER = (TOT + NTHR - 1) / NTHR;
     vec8<T> v[PER];
@@ -146,6 +146,7 @@ struct Prefetch {
     template <bool SWZ = false>
     __device__ __forceinline__ void store(T* const* dst, float* nrm, int norm_mask, int t0, int t_end) const {
         constexpr int RS = LdsTile<T, D>::RS;
+        const bool full = t0 + ROWS <= t_end;  // uniform: no row needs zeroing
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int c = threadIdx.x + i * NTHR;
@@ -153,7 +154,8 @@ struct Prefetch {
                 int tn, cc;
                 where(i, tn, cc);
                 const int row = cc / CPR, col = 8 * (cc % CPR);
-                const vec8<T> x = (t0 + row < t_end) ? v[i] : zero8<T>();
+                vec8<T> x = v[i];
+                if (!full && t0 + row >= t_end) x = zero8<T>();
                 // a select over constant indices (not dst[tn]) keeps the LDS
                 // address space visible to the compiler: no flat stores
                 T* d = dst[0];
@@ -170,7 +172,7 @@ struct Prefetch {
                         ss += xf * xf;
                     }
                     ss = group_sum<CPR>(ss);
-                    if (col == 0) nrm[tn * 32 + row] = -0.5f * kLog2e * ss;
+                    if (col == 0) nrm[tn * ROWS + row] = -0.5f * kLog2e * ss;
                 }
             }
         }
@@ -201,12 +203,30 @@ __device__ __forceinline__ vec8<T> omega_operand(const float* om_head, int f, in
 }
 
 // ---------------------------------------------------------------------------
+// Segment sums (partials, causal carries) of one (head, segment) in the
+// matrix-core result layout, so that every lane moves 16 aligned bytes:
+//   V part: ((ft * D/16 + nt) * 64 + lane) * 4 + i holds S[16 ft + 4 g + i][16 nt + r]
+//   z part: m * D + f holds S[f][D] (the sum of phi)
+// m (D + 1) floats in all.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ size_t seg_v_off(int ft, int nt, int lane) {
+    return ((size_t)(ft * (D / 16) + nt) * 64 + lane) * 4;
+}
+
+// ---------------------------------------------------------------------------
 // kv_partial: one workgroup (8 waves) per (segment, head, group of <= 256
-// features).  Wave w owns 32 features.  Tiles of 32 tokens are prefetched two
-// ahead into registers, stored into one of two LDS slots (one barrier per
-// tile).  Per tile: projection D[T x F] = K Omega'^T, a lazily raised shift M
-// (a lane-local test; the wave-wide max only when some lane exceeds M + kTau),
-// phi as the A operand, [V | 1] in kappa order through transpose reads.
+// features).  Wave w owns 32 features.  Steps of 64 tokens are prefetched PD
+// ahead into registers and staged into one of three LDS slots (one barrier
+// per step).  The loop is software-pipelined: while step i's features are
+// exponentiated and accumulated, step i+1's projection is already issued, so
+// matrix-core and vector work of one wave overlap.
+// Projection D[T x F] = K Omega'^T with the accumulator initialised to
+// -log2(e)|k|^2/2 - M: values are relative to the wave's shift M, which is
+// set from the first step's maximum and afterwards raised lazily (a
+// lane-local test; the wave-wide max only when some value exceeds kTau), with
+// exact rescaling of the sums.  phi is the A operand and [V | 1] (kappa
+// order, transpose reads) the B operand of the update.
 // Output: partial[bh][seg][f][0..D] (column D = sum of phi), pmax[bh][seg][f/32].
 // ---------------------------------------------------------------------------
 template <typename T, int D, int PD>
@@ -220,8 +240,10 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
     constexpr int NT = D / 16 + 1;
     constexpr int FW = 32;
     constexpr int NFT = FW / 16;
-    __shared__ __attribute__((aligned(16))) T tiles[2][2][TL::ELEMS];
-    __shared__ float norms[2][32];
+    constexpr int ST = 64;         // tokens per step
+    constexpr int TILE = ST * RS;  // elements of one staged tensor
+    __shared__ __attribute__((aligned(16))) T tiles[3][2][TILE];
+    __shared__ float norms[3][ST];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
     const int seg = blockIdx.x, bh = blockIdx.y, h = bh % H;
@@ -232,7 +254,7 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
     const bool active = f0 < m;
     const int t_begin = seg * seg_len;
     const int t_end = min(L, t_begin + seg_len);
-    const int ntiles = (t_end - t_begin + 31) / 32;
+    const int nsteps = (t_end - t_begin + ST - 1) / ST;
     const size_t xbase = (size_t)bh * L * D;
     const float* omh = omega + (om_per_head ? (size_t)h * m * D : 0);
 
@@ -247,77 +269,115 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
     for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) kv[ft][nt] = f4splat(0.0f);
-    float M = kNegInf;
+    float M = 0.0f;
 
     const T* src[2] = {k + xbase, v + xbase};
-    // PD tiles in flight in registers (global latency), two LDS slots.  Every
-    // unrolled step stores, loads and meets the barrier (loads past the last
-    // tile re-read it, from cache), so the load count is static.
-    Prefetch<T, D, 512, 2> pf[PD];
+    // PD steps in flight in registers (global latency).  Every unrolled step
+    // stores, loads and meets the barrier (loads past the last step re-read
+    // it, from cache), so the load count is static.
+    Prefetch<T, D, 512, 2, ST> pf[PD];
 #pragma unroll
-    for (int u = 0; u < PD; ++u) pf[u].load(src, t_begin + 32 * min(u, ntiles - 1), L - 1);
+    for (int u = 0; u < PD; ++u) pf[u].load(src, t_begin + ST * min(u, nsteps - 1), L - 1);
 
-    for (int it0 = 0; it0 < ntiles; it0 += PD) {
+    auto stage = [&](Prefetch<T, D, 512, 2, ST>& pr, int step) {
+        const int sl = step % 3;
+        T* dst[2] = {tiles[sl][0], tiles[sl][1]};
+        pr.store(dst, norms[sl], 1, t_begin + ST * min(step, nsteps - 1), step < nsteps ? t_end : -1);
+        pr.load(src, t_begin + ST * min(step + PD, nsteps - 1), L - 1);
+    };
+    // projection of one step (p = exponent - M) and its lane-local maximum
+    auto project = [&](int step, f4 (&p)[4][NFT]) -> float {
+        const int sl = step % 3;
+        const int t0 = t_begin + ST * step;
+        const bool full = t0 + ST <= t_end;
+        const T* kt = tiles[sl][0];
+        float lm = kNegInf;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f4 init = *reinterpret_cast<const f4*>(&norms[sl][16 * tt + 4 * g]) - M;
+            if (!full) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (t0 + 16 * tt + 4 * g + i >= t_end) init[i] = kNegInf;
+            }
+            vec8<T> x[KSD];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) x[ks] = row_operand<T, D>(kt, 16 * tt + r, ks, g);
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) {
+                p[tt][ft] = init;
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) p[tt][ft] = mma32(x[ks], om[ft][ks], p[tt][ft]);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lm = __builtin_fmaxf(lm, p[tt][ft][i]);
+        return lm;
+    };
+
+    // step 0: stage, project, and take its maximum as the shift
+    f4 pc[4][NFT];
+    stage(pf[0], 0);
+    __syncthreads();
+    if (active) {
+        const float tm = wave_max_uniform(project(0, pc));
+        M = tm;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) pc[tt][ft] -= tm;
+    }
+
+    for (int i0 = 0; i0 < nsteps; i0 += PD) {
 #pragma unroll
         for (int u = 0; u < PD; ++u) {
-            const int it = it0 + u;
-            {
-                const int slot = it & 1;
-                T* dst[2] = {tiles[slot][0], tiles[slot][1]};
-                pf[u].store(dst, norms[slot], 1, t_begin + 32 * min(it, ntiles - 1), it < ntiles ? t_end : -1);
-                pf[u].load(src, t_begin + 32 * min(it + PD, ntiles - 1), L - 1);
-                __syncthreads();
-                if (active && it < ntiles) {
-                    const int t0 = t_begin + 32 * it;
-                    const T* kt = tiles[slot][0];
-                    const T* vt = tiles[slot][1];
-                    f4 p[2][NFT];
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        f4 init = *reinterpret_cast<const f4*>(&norms[slot][16 * tt + 4 * g]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (t0 + 16 * tt + 4 * g + i >= t_end) init[i] = kNegInf;
-                        vec8<T> x[KSD];
-#pragma unroll
-                        for (int ks = 0; ks < KSD; ++ks) x[ks] = row_operand<T, D>(kt, 16 * tt + r, ks, g);
-#pragma unroll
-                        for (int ft = 0; ft < NFT; ++ft) {
-                            p[tt][ft] = init;
-#pragma unroll
-                            for (int ks = 0; ks < KSD; ++ks) p[tt][ft] = mma32(x[ks], om[ft][ks], p[tt][ft]);
-                        }
-                    }
-                    float lm = kNegInf;
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) lm = __builtin_fmaxf(lm, p[tt][ft][i]);
-                    if (wave_any(lm > M + kTau)) {
-                        const float tm = wave_max_uniform(lm);
-                        const float sc = (M == kNegInf) ? 0.0f : exp2f_fast(M - tm);
+            const int it = i0 + u;
+            stage(pf[(u + 1) % PD], it + 1);
+            __syncthreads();
+            if (active && it < nsteps) {
+                // next step's projection first (independent of this step's update)
+                f4 pn[4][NFT];
+                if (it + 1 < nsteps) {
+                    const float lm = project(it + 1, pn);
+                    if (wave_any(lm > kTau)) {
+                        const float tm = wave_max_uniform(lm);  // raise M by tm
+                        const float sc = exp2f_fast(-tm);
 #pragma unroll
                         for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
                             for (int nt = 0; nt < NT; ++nt) kv[ft][nt] *= sc;
-                        M = tm;
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                            for (int ft = 0; ft < NFT; ++ft) {
+                                pc[tt][ft] -= tm;
+                                pn[tt][ft] -= tm;
+                            }
+                        M += tm;
                     }
+                }
+                const T* vt = tiles[it % 3][1];
+#pragma unroll
+                for (int ks2 = 0; ks2 < 2; ++ks2) {  // tokens 32 ks2 .. 32 ks2 + 31
                     vec8<T> a[NFT];
 #pragma unroll
                     for (int ft = 0; ft < NFT; ++ft) {
                         f4 e0, e1;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            e0[i] = exp2f_fast(p[0][ft][i] - M);
-                            e1[i] = exp2f_fast(p[1][ft][i] - M);
+                            e0[i] = exp2f_fast(pc[2 * ks2][ft][i]);
+                            e1[i] = exp2f_fast(pc[2 * ks2 + 1][ft][i]);
                         }
                         a[ft] = pack8t<T>(e0, e1);
                     }
+                    const T* vk = vt + 32 * ks2 * RS;
 #pragma unroll
                     for (int nt = 0; nt < NT - 1; ++nt) {
-                        const vec8<T> vb = kappa_col<RS>(vt, 16 * nt, lane);
+                        const vec8<T> vb = kappa_col<RS>(vk, 16 * nt, lane);
 #pragma unroll
                         for (int ft = 0; ft < NFT; ++ft) kv[ft][nt] = mma32(a[ft], vb, kv[ft][nt]);
                     }
@@ -325,6 +385,10 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
 #pragma unroll
                     for (int ft = 0; ft < NFT; ++ft) kv[ft][NT - 1] = mma32(a[ft], ones, kv[ft][NT - 1]);
                 }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int ft = 0; ft < NFT; ++ft) pc[tt][ft] = pn[tt][ft];
             }
         }
     }
@@ -332,122 +396,121 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
     if (!active) return;
     float* pp = partial + ((size_t)bh * nseg + seg) * (size_t)m * (D + 1);
 #pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
+    for (int ft = 0; ft < NFT; ++ft) {
+        const int fg = f0 / 16 + ft;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int f = f0 + 16 * ft + 4 * g + i;
-#pragma unroll
-            for (int nt = 0; nt < NT - 1; ++nt) pp[(size_t)f * (D + 1) + 16 * nt + r] = kv[ft][nt][i];
-            if (r == 0) pp[(size_t)f * (D + 1) + D] = kv[ft][NT - 1][i];
-        }
+        for (int nt = 0; nt < NT - 1; ++nt) *reinterpret_cast<f4*>(pp + seg_v_off<D>(fg, nt, lane)) = kv[ft][nt];
+        if (r == 0) *reinterpret_cast<f4*>(pp + (size_t)m * D + 16 * fg + 4 * g) = kv[ft][NT - 1];
+    }
     if (lane == 0) pmax[((size_t)bh * nseg + seg) * (m / 32) + f0 / 32] = M;
 }
 
 // ---------------------------------------------------------------------------
-// merge_scan: one workgroup per (32-feature block, head, column slice).
+// merge_scan: one workgroup per (32-feature block, head); thread (mt, lane)
+// owns one result tile column: mt < D/16 a value tile, mt = D/16 the z row.
 // mode 0 (bidirectional): sum over the segment partials, rescaled to the
 //   block's maximum shift; written as the packed A operand of the output
 //   contraction (kvpack[bh][mt][fb][lane], kappa order over the block's 32
 //   features; mt = D/16 is the z row replicated) and mmax[bh][fb].
 // mode 1 (causal): carry[bh][s] = sum over segments s' < s, scaled to
 //   cmax[bh][s][fb] = max over s' <= s of the partial shifts (every key of
-//   segment s has exponents <= cmax + kTau: the chunk kernel's fixed shift).
+//   segment s has exponents <= cmax + kTau), in the segment-sum layout.
 // Both modes also pack log2(e) Omega for the block's 32 features (A-operand
 // order of the projection D[F x T]) into ompack, once per projection.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256) void merge_scan_kernel(const float* __restrict__ partial, const float* __restrict__ pmax,
-                                                         const float* __restrict__ omega, int om_per_head, int H, int m,
-                                                         int nseg, int mode, vec8<T>* __restrict__ kvpack,
-                                                         float* __restrict__ mmax, float* __restrict__ carry,
-                                                         float* __restrict__ cmax, vec8<T>* __restrict__ ompack) {
-    constexpr int D1 = D + 1;
+__global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
+    const float* __restrict__ partial, const float* __restrict__ pmax, const float* __restrict__ omega, int om_per_head,
+    int H, int m, int nseg, int mode, vec8<T>* __restrict__ kvpack, float* __restrict__ mmax,
+    float* __restrict__ carry, float* __restrict__ cmax, vec8<T>* __restrict__ ompack) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
-    const int fb = blockIdx.x, bh = blockIdx.y, cs = blockIdx.z, ncs = gridDim.z;
+    constexpr int NTV = D / 16;
+    constexpr int NMT = NTV + 1;
+    const int fb = blockIdx.x, bh = blockIdx.y;
     const int h = bh % H, b = bh / H;
     const int nfb = m / 32;
-    const int c_lo = (D1 * cs) / ncs, c_hi = (D1 * (cs + 1)) / ncs;  // this workgroup's columns
-    const int ncol = c_hi - c_lo;
-    const float* pb = partial + (size_t)bh * nseg * m * D1;
+    const int mt = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const size_t seg_stride = (size_t)m * (D + 1);
+    const float* pb = partial + (size_t)bh * nseg * seg_stride;
     const float* pm = pmax + (size_t)bh * nseg * nfb;
 
-    if (cs == 0 && b == 0 && (om_per_head || h == 0)) {
+    if (b == 0 && (om_per_head || h == 0)) {
         const float* omh = omega + (om_per_head ? (size_t)h * m * D : 0);
         vec8<T>* dst = ompack + (size_t)(om_per_head ? h : 0) * (m / 16) * KSD * 64;
         for (int e = threadIdx.x; e < 2 * KSD * 64; e += blockDim.x) {
-            const int lane = e % 64, ks = (e / 64) % KSD, ft = 2 * fb + e / (64 * KSD);
-            dst[((size_t)ft * KSD + ks) * 64 + lane] = omega_operand<T, D>(omh, 16 * ft + (lane & 15), ks, lane >> 4);
+            const int ln = e % 64, ks = (e / 64) % KSD, ft = 2 * fb + e / (64 * KSD);
+            dst[((size_t)ft * KSD + ks) * 64 + ln] = omega_operand<T, D>(omh, 16 * ft + (ln & 15), ks, ln >> 4);
         }
     }
 
+    // this thread's two 4-float pieces (feature tiles 2 fb, 2 fb + 1) of a segment
+    const size_t o0 = mt < NTV ? seg_v_off<D>(2 * fb, mt, lane) : (size_t)m * D + 32 * fb + 4 * g;
+    const size_t o1 = mt < NTV ? seg_v_off<D>(2 * fb + 1, mt, lane) : (size_t)m * D + 32 * fb + 16 + 4 * g;
+    constexpr int NB = 8;  // segments loaded per batch
+
     if (mode == 0) {
-        __shared__ float merged[32 * D1];
         float Ms = kNegInf;
         for (int s = 0; s < nseg; ++s) Ms = __builtin_fmaxf(Ms, pm[(size_t)s * nfb + fb]);
-        for (int e = threadIdx.x; e < 32 * ncol; e += blockDim.x) {
-            const int f = 32 * fb + e / ncol, c = c_lo + e % ncol;
-            const float* src = pb + (size_t)f * D1 + c;
-            float acc = 0.0f;
-            for (int s0 = 0; s0 < nseg; s0 += 8) {
-                float x[8], sc[8];
+        f4 a0 = f4splat(0.0f), a1 = f4splat(0.0f);
+        for (int s0 = 0; s0 < nseg; s0 += NB) {
+            f4 x0[NB], x1[NB];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {  // eight independent loads in flight
-                    const int s = s0 + j;
-                    const float ms = s < nseg ? pm[(size_t)s * nfb + fb] : kNegInf;
-                    x[j] = s < nseg ? src[(size_t)s * m * D1] : 0.0f;
-                    sc[j] = ms == kNegInf ? 0.0f : exp2f_fast(ms - Ms);
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc += sc[j] * x[j];
+            for (int j = 0; j < NB; ++j) {  // independent loads in flight
+                const int s = min(s0 + j, nseg - 1);
+                x0[j] = *reinterpret_cast<const f4*>(pb + (size_t)s * seg_stride + o0);
+                x1[j] = *reinterpret_cast<const f4*>(pb + (size_t)s * seg_stride + o1);
             }
-            merged[(e / ncol) * D1 + c] = acc;
-        }
-        __syncthreads();
-        constexpr int NMT = D / 16 + 1;
-        for (int e = threadIdx.x; e < NMT * 64; e += blockDim.x) {
-            const int mt = e / 64, lane = e % 64, r = lane & 15, g = lane >> 4;
-            const int col = mt < NMT - 1 ? 16 * mt + r : D;
-            if (col < c_lo || col >= c_hi) continue;
-            vec8<T> v;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int fl = j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-                v[j] = (T)merged[fl * D1 + col];
+            for (int j = 0; j < NB; ++j) {
+                const float ms = s0 + j < nseg ? pm[(size_t)(s0 + j) * nfb + fb] : kNegInf;
+                const float sc = ms == kNegInf ? 0.0f : exp2f_fast(ms - Ms);
+                a0 += sc * x0[j];
+                a1 += sc * x1[j];
             }
-            kvpack[(((size_t)bh * NMT + mt) * nfb + fb) * 64 + lane] = v;
         }
-        if (threadIdx.x == 0 && cs == 0) mmax[(size_t)bh * nfb + fb] = Ms;
+        kvpack[(((size_t)bh * NMT + mt) * nfb + fb) * 64 + lane] = pack8t<T>(a0, a1);
+        if (threadIdx.x == 0) mmax[(size_t)bh * nfb + fb] = Ms;
     } else {
-        float* cb = carry + (size_t)bh * nseg * m * D1;
-        for (int e = threadIdx.x; e < 32 * ncol; e += blockDim.x) {
-            const int f = 32 * fb + e / ncol, c = c_lo + e % ncol;
-            const float* src = pb + (size_t)f * D1 + c;
-            float* dst = cb + (size_t)f * D1 + c;
-            float acc = 0.0f, Mrun = kNegInf;
-            for (int s0 = 0; s0 < nseg; s0 += 8) {
-                float x[8];
+        float* cb = carry + (size_t)bh * nseg * seg_stride;
+        const bool writer = mt < NTV || r == 0;  // the z row: one lane per 4 features
+        f4 a0 = f4splat(0.0f), a1 = f4splat(0.0f);
+        float Mrun = kNegInf;
+        for (int s0 = 0; s0 < nseg; s0 += NB) {
+            f4 x0[NB], x1[NB];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = s0 + j < nseg ? src[(size_t)(s0 + j) * m * D1] : 0.0f;
+            for (int j = 0; j < NB; ++j) {
+                const int s = min(s0 + j, nseg - 1);
+                x0[j] = *reinterpret_cast<const f4*>(pb + (size_t)s * seg_stride + o0);
+                x1[j] = *reinterpret_cast<const f4*>(pb + (size_t)s * seg_stride + o1);
+            }
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int s = s0 + j;
-                    if (s < nseg) {
-                        const float ms = pm[(size_t)s * nfb + fb];
-                        if (ms > Mrun) {
-                            acc = (Mrun == kNegInf) ? 0.0f : acc * exp2f_fast(Mrun - ms);
-                            Mrun = ms;
-                        }
-                        dst[(size_t)s * m * D1] = acc;
-                        if (ms != kNegInf) acc += exp2f_fast(ms - Mrun) * x[j];
+            for (int j = 0; j < NB; ++j) {
+                const int s = s0 + j;
+                if (s < nseg) {
+                    const float ms = pm[(size_t)s * nfb + fb];
+                    if (ms > Mrun) {
+                        const float sc = Mrun == kNegInf ? 0.0f : exp2f_fast(Mrun - ms);
+                        a0 *= sc;
+                        a1 *= sc;
+                        Mrun = ms;
+                    }
+                    if (writer) {
+                        *reinterpret_cast<f4*>(cb + (size_t)s * seg_stride + o0) = a0;
+                        *reinterpret_cast<f4*>(cb + (size_t)s * seg_stride + o1) = a1;
+                    }
+                    if (ms != kNegInf) {
+                        const float sc = exp2f_fast(ms - Mrun);
+                        a0 += sc * x0[j];
+                        a1 += sc * x1[j];
                     }
                 }
             }
         }
-        if (threadIdx.x == 0 && cs == 0) {
-            float Mrun = kNegInf;
+        if (threadIdx.x == 0) {
+            float Mr = kNegInf;
             for (int s = 0; s < nseg; ++s) {
-                Mrun = __builtin_fmaxf(Mrun, pm[(size_t)s * nfb + fb]);
-                cmax[((size_t)bh * nseg + s) * nfb + fb] = Mrun;
+                Mr = __builtin_fmaxf(Mr, pm[(size_t)s * nfb + fb]);
+                cmax[((size_t)bh * nseg + s) * nfb + fb] = Mr;
             }
         }
     }
@@ -726,14 +789,12 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
         for (int ft = 0; ft < NFT; ++ft) {
             const float mb = cm[(f0 + 16 * ft) / 32];
             const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - M);
+            const int fg = f0 / 16 + ft;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int f = f0 + 16 * ft + 4 * g + i;
-                    const int c = nt < NT - 1 ? 16 * nt + r : D;
-                    G[ft][nt][i] = sc * cb[(size_t)f * D1 + c];
-                }
+            for (int nt = 0; nt < NT; ++nt) {
+                const size_t o = nt < NT - 1 ? seg_v_off<D>(fg, nt, lane) : (size_t)m * D + 16 * fg + 4 * g;
+                G[ft][nt] = sc * *reinterpret_cast<const f4*>(cb + o);
+            }
         }
     }
 
@@ -985,8 +1046,7 @@ __global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restr
         for (int ft = 0; ft < NFT; ++ft) {
             const float mb = cm[ft / 2];
             const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) G[ft][i] = sc * cb[(size_t)(16 * ft + 4 * g + i) * D1 + 16 * w + r];
+            G[ft] = sc * *reinterpret_cast<const f4*>(cb + seg_v_off<D>(ft, w, lane));
         }
 #pragma unroll
         for (int zb = 0; zb < ZB; ++zb) {
@@ -996,9 +1056,8 @@ __global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restr
             const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Z[2 * zb + hf][i] = own ? sc * cb[(size_t)(32 * kb + 16 * hf + 4 * g + i) * D1 + D] : 0.0f;
+                Z[2 * zb + hf] = own ? sc * *reinterpret_cast<const f4*>(cb + (size_t)M * D + 32 * kb + 16 * hf + 4 * g)
+                                     : f4splat(0.0f);
         }
     }
 
@@ -1299,14 +1358,13 @@ static hipError_t launch_all(const LaunchArgs& a) {
     const int per_head = a.omega_per_head ? 1 : 0;
     const int nfg = (a.m + 255) / 256;
     stage_event(a, 0);
-    constexpr int PD_KV = D >= 128 ? 3 : 6;
+    constexpr int PD_KV = D >= 128 ? 1 : 3;
     hipLaunchKernelGGL((kv_partial_kernel<T, D, PD_KV>), dim3(a.nseg, BH, nfg), dim3(512), 0, st, k, v, a.omega, per_head,
                        a.ws_partial, a.ws_pmax, a.H, a.L, a.m, a.seg_len, a.nseg);
     stage_event(a, 1);
     const int nfb = a.m / 32;
-    const int ncs = std::max(1, std::min((D + 1) / 8, (1024 + nfb * BH - 1) / (nfb * BH)));
     const int mode = a.op == OpKind::Bidir ? 0 : 1;
-    hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(nfb, BH, ncs), dim3(256), 0, st, a.ws_partial, a.ws_pmax,
+    hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(nfb, BH), dim3(64 * (D / 16 + 1)), 0, st, a.ws_partial, a.ws_pmax,
                        a.omega, per_head, a.H, a.m, a.nseg, mode, reinterpret_cast<vec8<T>*>(a.ws_kvpack), a.ws_mmax,
                        a.ws_carry, a.ws_cmax, ompack);
     stage_event(a, 2);
