@@ -104,6 +104,26 @@ template <typename V> __device__ __forceinline__ V gload_vec(const V* p) {
     return *(__attribute__((address_space(1))) const V*)(p);
 }
 
+// Workgroup copy of n 16-byte vectors from global memory to LDS, with the
+// loads of a batch issued before any of its stores (one memory latency per
+// batch instead of one per vector).
+template <int NTHR, int BATCH = 8, typename V>
+__device__ __forceinline__ void copy_to_lds(V* dst, const V* src, int n) {
+    for (int e0 = 0; e0 < n; e0 += NTHR * BATCH) {
+        V x[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int e = e0 + j * NTHR + (int)threadIdx.x;
+            if (e < n) x[j] = gload_vec(src + e);
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int e = e0 + j * NTHR + (int)threadIdx.x;
+            if (e < n) dst[e] = x[j];
+        }
+    }
+}
+
 // Lane exchanges (ds_bpermute through __shfl_xor).
 // Sum / max over the four lanes r, r+16, r+32, r+48 (the lanes holding one
 // token column in B-operand layout).

@@ -406,12 +406,14 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
 }
 
 // ---------------------------------------------------------------------------
-// merge_scan: one workgroup per (32-feature block, head); thread (mt, lane)
-// owns one result tile column: mt < D/16 a value tile, mt = D/16 the z row.
+// merge_scan: one workgroup per (32-feature block, head, half); thread
+// (mt, lane) owns one 4-float piece of a result tile: feature tile
+// 2 fb + half, and mt < D/16 a value tile or mt = D/16 the z row.
 // mode 0 (bidirectional): sum over the segment partials, rescaled to the
 //   block's maximum shift; written as the packed A operand of the output
 //   contraction (kvpack[bh][mt][fb][lane], kappa order over the block's 32
-//   features; mt = D/16 is the z row replicated) and mmax[bh][fb].
+//   features, this half filling slots 4 half .. 4 half + 3; mt = D/16 is the
+//   z row replicated) and mmax[bh][fb].
 // mode 1 (causal): carry[bh][s] = sum over segments s' < s, scaled to
 //   cmax[bh][s][fb] = max over s' <= s of the partial shifts (every key of
 //   segment s has exponents <= cmax + kTau), in the segment-sum layout.
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
     constexpr int KSD = D < 32 ? 1 : D / 32;
     constexpr int NTV = D / 16;
     constexpr int NMT = NTV + 1;
-    const int fb = blockIdx.x, bh = blockIdx.y;
+    const int fb = blockIdx.x, bh = blockIdx.y, half = blockIdx.z;
     const int h = bh % H, b = bh / H;
     const int nfb = m / 32;
     const int mt = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
@@ -437,76 +439,64 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
     if (b == 0 && (om_per_head || h == 0)) {
         const float* omh = omega + (om_per_head ? (size_t)h * m * D : 0);
         vec8<T>* dst = ompack + (size_t)(om_per_head ? h : 0) * (m / 16) * KSD * 64;
-        for (int e = threadIdx.x; e < 2 * KSD * 64; e += blockDim.x) {
-            const int ln = e % 64, ks = (e / 64) % KSD, ft = 2 * fb + e / (64 * KSD);
+        for (int e = threadIdx.x; e < KSD * 64; e += blockDim.x) {
+            const int ln = e % 64, ks = e / 64, ft = 2 * fb + half;
             dst[((size_t)ft * KSD + ks) * 64 + ln] = omega_operand<T, D>(omh, 16 * ft + (ln & 15), ks, ln >> 4);
         }
     }
 
-    // this thread's two 4-float pieces (feature tiles 2 fb, 2 fb + 1) of a segment
-    const size_t o0 = mt < NTV ? seg_v_off<D>(2 * fb, mt, lane) : (size_t)m * D + 32 * fb + 4 * g;
-    const size_t o1 = mt < NTV ? seg_v_off<D>(2 * fb + 1, mt, lane) : (size_t)m * D + 32 * fb + 16 + 4 * g;
+    // this thread's 4-float piece of a segment sum
+    const int ft = 2 * fb + half;
+    const size_t o = mt < NTV ? seg_v_off<D>(ft, mt, lane) : (size_t)m * D + 16 * ft + 4 * g;
     constexpr int NB = 8;  // segments loaded per batch
 
     if (mode == 0) {
         float Ms = kNegInf;
         for (int s = 0; s < nseg; ++s) Ms = __builtin_fmaxf(Ms, pm[(size_t)s * nfb + fb]);
-        f4 a0 = f4splat(0.0f), a1 = f4splat(0.0f);
+        f4 acc = f4splat(0.0f);
         for (int s0 = 0; s0 < nseg; s0 += NB) {
-            f4 x0[NB], x1[NB];
+            f4 x[NB];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {  // independent loads in flight
-                const int s = min(s0 + j, nseg - 1);
-                x0[j] = *reinterpret_cast<const f4*>(pb + (size_t)s * seg_stride + o0);
-                x1[j] = *reinterpret_cast<const f4*>(pb + (size_t)s * seg_stride + o1);
-            }
+            for (int j = 0; j < NB; ++j)  // independent loads in flight
+                x[j] = *reinterpret_cast<const f4*>(pb + (size_t)min(s0 + j, nseg - 1) * seg_stride + o);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const float ms = s0 + j < nseg ? pm[(size_t)(s0 + j) * nfb + fb] : kNegInf;
-                const float sc = ms == kNegInf ? 0.0f : exp2f_fast(ms - Ms);
-                a0 += sc * x0[j];
-                a1 += sc * x1[j];
+                acc += (ms == kNegInf ? 0.0f : exp2f_fast(ms - Ms)) * x[j];
             }
         }
-        kvpack[(((size_t)bh * NMT + mt) * nfb + fb) * 64 + lane] = pack8t<T>(a0, a1);
-        if (threadIdx.x == 0) mmax[(size_t)bh * nfb + fb] = Ms;
+        typedef __attribute__((ext_vector_type(4))) T T4;
+        T4 packed;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) packed[i] = (T)acc[i];
+        T4* dst = reinterpret_cast<T4*>(kvpack + (((size_t)bh * NMT + mt) * nfb + fb) * 64 + lane) + half;
+        *dst = packed;
+        if (threadIdx.x == 0 && half == 0) mmax[(size_t)bh * nfb + fb] = Ms;
     } else {
         float* cb = carry + (size_t)bh * nseg * seg_stride;
         const bool writer = mt < NTV || r == 0;  // the z row: one lane per 4 features
-        f4 a0 = f4splat(0.0f), a1 = f4splat(0.0f);
+        f4 acc = f4splat(0.0f);
         float Mrun = kNegInf;
         for (int s0 = 0; s0 < nseg; s0 += NB) {
-            f4 x0[NB], x1[NB];
+            f4 x[NB];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const int s = min(s0 + j, nseg - 1);
-                x0[j] = *reinterpret_cast<const f4*>(pb + (size_t)s * seg_stride + o0);
-                x1[j] = *reinterpret_cast<const f4*>(pb + (size_t)s * seg_stride + o1);
-            }
+            for (int j = 0; j < NB; ++j)
+                x[j] = *reinterpret_cast<const f4*>(pb + (size_t)min(s0 + j, nseg - 1) * seg_stride + o);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int s = s0 + j;
                 if (s < nseg) {
                     const float ms = pm[(size_t)s * nfb + fb];
                     if (ms > Mrun) {
-                        const float sc = Mrun == kNegInf ? 0.0f : exp2f_fast(Mrun - ms);
-                        a0 *= sc;
-                        a1 *= sc;
+                        acc *= (Mrun == kNegInf ? 0.0f : exp2f_fast(Mrun - ms));
                         Mrun = ms;
                     }
-                    if (writer) {
-                        *reinterpret_cast<f4*>(cb + (size_t)s * seg_stride + o0) = a0;
-                        *reinterpret_cast<f4*>(cb + (size_t)s * seg_stride + o1) = a1;
-                    }
-                    if (ms != kNegInf) {
-                        const float sc = exp2f_fast(ms - Mrun);
-                        a0 += sc * x0[j];
-                        a1 += sc * x1[j];
-                    }
+                    if (writer) *reinterpret_cast<f4*>(cb + (size_t)s * seg_stride + o) = acc;
+                    if (ms != kNegInf) acc += exp2f_fast(ms - Mrun) * x[j];
                 }
             }
         }
-        if (threadIdx.x == 0) {
+        if (threadIdx.x == 0 && half == 0) {
             float Mr = kNegInf;
             for (int s = 0; s < nseg; ++s) {
                 Mr = __builtin_fmaxf(Mr, pm[(size_t)s * nfb + fb]);
@@ -531,7 +521,7 @@ __global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q,
                                                         int L, int m) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
     constexpr int NMT = D / 16 + 1;
-    constexpr int NTT = D >= 128 ? 2 : 4;  // query tiles per wave
+    constexpr int NTT = 2;  // query tiles per wave
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     const int nft = m / 16, nfb = m / 32;
     vec8<T>* kv_stage = reinterpret_cast<vec8<T>*>(smem_raw);
@@ -555,10 +545,8 @@ __global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q,
     }
     const vec8<T>* omh = ompack + (size_t)(om_head_vecs ? h : 0) * (size_t)om_head_vecs;
     const vec8<T>* kvh = kvpack + (size_t)bh * NMT * nfb * 64;
-    if (OM_LDS)
-        for (int e = threadIdx.x; e < nft * KSD * 64; e += blockDim.x) om_stage[e] = omh[e];
-    if (KV_LDS)
-        for (int e = threadIdx.x; e < NMT * nfb * 64; e += blockDim.x) kv_stage[e] = kvh[e];
+    if (OM_LDS) copy_to_lds<512>(om_stage, omh, nft * KSD * 64);
+    if (KV_LDS) copy_to_lds<512>(kv_stage, kvh, NMT * nfb * 64);
     const vec8<T>* om_src = OM_LDS ? om_stage : omh;
     const vec8<T>* kv_src = KV_LDS ? kv_stage : kvh;
     float Mstar = kNegInf;
@@ -1029,7 +1017,7 @@ __global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restr
     // projection operands of this head into LDS
     {
         const bf16x8* omh = ompack + (size_t)(om_head_vecs ? h : 0) * (size_t)om_head_vecs;
-        for (int e = threadIdx.x; e < NFT * KSD * 64; e += 256) om[e] = omh[e];
+        copy_to_lds<256>(om, omh, NFT * KSD * 64);
     }
 
     // carry-in: state slice for columns 16w.. and z for this wave's blocks,
@@ -1364,12 +1352,12 @@ static hipError_t launch_all(const LaunchArgs& a) {
     stage_event(a, 1);
     const int nfb = a.m / 32;
     const int mode = a.op == OpKind::Bidir ? 0 : 1;
-    hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(nfb, BH), dim3(64 * (D / 16 + 1)), 0, st, a.ws_partial, a.ws_pmax,
+    hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(nfb, BH, 2), dim3(64 * (D / 16 + 1)), 0, st, a.ws_partial, a.ws_pmax,
                        a.omega, per_head, a.H, a.m, a.nseg, mode, reinterpret_cast<vec8<T>*>(a.ws_kvpack), a.ws_mmax,
                        a.ws_carry, a.ws_cmax, ompack);
     stage_event(a, 2);
     if (a.op == OpKind::Bidir) {
-        constexpr int NTT = D >= 128 ? 2 : 4;
+        constexpr int NTT = 2;
         const int tok_per_wg = 8 * 16 * NTT;
         const int blocks = (a.L + tok_per_wg - 1) / tok_per_wg;
         const size_t om_b = sizeof(vec8<T>) * 64 * (size_t)(a.m / 16) * KSD;
