@@ -30,8 +30,9 @@ from positive_random_feature_amd import _lib  # noqa: E402
 from positive_random_feature_amd.workloads import WORKLOADS, make_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-STAGES = {"bidir": ["kv_partial", "merge", "bidir_out"],
-          "causal": ["kv_partial", "scan", "causal_chunk"]}
+# kernels of the three stages of each op at the bench shapes (d=64, m=256)
+STAGES = {"bidir": ["kv_partial", "merge_scan", "bidir_out"],
+          "causal": ["kv_partial", "merge_scan", "causal_tile"]}
 KERNEL_SOURCES = ["positive_random_feature_amd/csrc/favor_kernels.hip", "positive_random_feature_amd/csrc/favor_device.h"]
 
 
@@ -118,15 +119,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, src_hash: str):
-    """HBM bytes per launch from the committed counter summary, or None when
-    it is missing or was taken on different kernel sources."""
+def traffic_for(stage: str, src_hash: str):
+    """HBM bytes per launch of a stage ("<workload>:<kernel>") from the
+    committed counter summary, or None when it is missing or was taken on
+    different kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    entry = t.get("kernels", {}).get(kernel)
+    entry = t.get("stages", {}).get(stage)
     if not entry or t.get("source_hash") != src_hash:
         return None
     return entry.get("bytes_per_launch")
@@ -141,13 +143,16 @@ def cpu_baseline(ops):
     for op in ops:
         inp = op.inp
         fn = native.bidir if op.w.op == "bidir" else native.causal
-        t0 = time.perf_counter()
-        fn(inp.q, inp.k, inp.v, op.omega_host)
-        t_total += time.perf_counter() - t0
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn(inp.q, inp.k, inp.v, op.omega_host)
+            runs.append(time.perf_counter() - t0)
+        t_total += sorted(runs)[1]
         tokens += op.w.tokens
     return {"value": tokens / t_total, "unit": "tokens/s", "cores": native.num_threads(), "kind": "oracle",
-            "sample": "one full step: bidir 4x8x4096 + causal 2x8x8192 (d=64, m=256), fp64 plain-C oracle, "
-                      "OpenMP over heads", "seconds": t_total}
+            "sample": "one full step (bidir 4x8x4096 + causal 2x8x8192, d=64, m=256), median of 3 runs per op, "
+                      "fp64 plain-C oracle, OpenMP over heads", "seconds": t_total}
 
 
 def main():
@@ -223,9 +228,9 @@ def main():
     dom_op = next(op for op in ops if dom.startswith(op.w.name + ":"))
     kname = dom.split(":")[1]
     elem = 2
-    per_token = {"causal_chunk": 4 * dom_op.w.d * elem,   # q, k, v read + out written
+    per_token = {"causal_tile": 4 * dom_op.w.d * elem,    # q, k, v read + out written
                  "bidir_out": 2 * dom_op.w.d * elem,      # q read + out written
-                 "kv_partial": 2 * dom_op.w.d * elem}.get(kname, 0)
+                 "kv_partial": 2 * dom_op.w.d * elem}.get(kname, 0)  # k, v read
     alg_bytes = per_token * dom_op.w.tokens
     dom_s = stage_ms[dom] * 1e-3
     achieved = alg_bytes / dom_s / 1e9 if dom_s > 0 else 0.0
@@ -245,10 +250,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian Q/K/V, seeded orthogonal projection)",
         "config": {"workload": "bidir B4 H8 L4096 d64 m256 (shared omega) + causal B2 H8 L8192 d64 m256 (omega per head)",
-                   "tokens_per_step": tokens_per_step, "chunk": 32},
+                   "tokens_per_step": tokens_per_step, "causal_chunk": 64},
         "roofline": {"bound": "hbm", "kernel": kname, "op": dom_op.w.name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_for(kname, src_hash), "alg_bytes_per_launch": alg_bytes,
+                     "traffic": traffic_for(dom, src_hash), "alg_bytes_per_launch": alg_bytes,
                      "avg_launch_ms": stage_ms[dom]},
         "per_op_tokens_per_s": {name: WORKLOADS[name].tokens / (ms * 1e-3) for name, ms in op_ms.items()},
         "stage_ms": stage_ms,

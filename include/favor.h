@@ -104,7 +104,9 @@ favor_status favor_bidir(const favor_shape *shape, const void *q, const void *k,
  * attention):
  *     out_t = phi(q_t)^T G_t / phi(q_t)^T (sum_{s<=t} phi(k_s)),
  * with an inclusive mask (position t attends to keys 0..t).
- * chunk: tokens per step of the chunked scan (0 = default 32; allowed 32).
+ * chunk: tokens per step of the chunked scan.  0 selects the library's
+ * length for the shape: 64 for bf16 with d = 64 and m <= 256, 32 otherwise;
+ * a nonzero value must equal that length (else FAVOR_ERR_UNSUPPORTED).
  * Workspace as for favor_bidir with FAVOR_OP_CAUSAL.
  */
 favor_status favor_causal(const favor_shape *shape, const void *q, const void *k, const void *v,

@@ -156,7 +156,8 @@ favor_status favor_bidir(const favor_shape* shape, const void* q, const void* k,
 
 favor_status favor_causal(const favor_shape* shape, const void* q, const void* k, const void* v, const float* omega,
                           void* out, int chunk, void* ws, size_t ws_bytes, void* stream) {
-    if (chunk != 0 && chunk != 32) return FAVOR_ERR_UNSUPPORTED;
+    if (chunk != 0 && shape && chunk != favor::causal_chunk_tokens(dtype_bytes(shape->dtype), shape->d, shape->m))
+        return FAVOR_ERR_UNSUPPORTED;
     return run(FAVOR_OP_CAUSAL, shape, q, k, v, omega, out, nullptr, nullptr, 0, ws, ws_bytes, stream);
 }
 
@@ -175,7 +176,8 @@ favor_status favor_causal_profiled(const favor_shape* shape, const void* q, cons
     if (!events || n_events < FAVOR_N_STAGES + 1) return FAVOR_ERR_INVALID_ARG;
     for (int i = 0; i <= FAVOR_N_STAGES; ++i)
         if (!events[i]) return FAVOR_ERR_INVALID_ARG;
-    if (chunk != 0 && chunk != 32) return FAVOR_ERR_UNSUPPORTED;
+    if (chunk != 0 && shape && chunk != favor::causal_chunk_tokens(dtype_bytes(shape->dtype), shape->d, shape->m))
+        return FAVOR_ERR_UNSUPPORTED;
     return run(FAVOR_OP_CAUSAL, shape, q, k, v, omega, out, nullptr, nullptr, 0, ws, ws_bytes, stream, events);
 }
 

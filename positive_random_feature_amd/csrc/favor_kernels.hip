@@ -23,8 +23,12 @@
 //   merge_scan      per (head, 32-feature block): total over segments
 //                   (bidirectional) or exclusive prefix (causal carry-in);
 //                   also packs log2(e) omega in operand order
-//   bidir_out       phi(q) . [KV | z] for tiles of 64 queries per wave
-//   causal_chunk    per (head, segment): chunked scan, 32 tokens per step
+//   bidir_out       phi(q) . [KV | z] for tiles of 32 queries per wave
+//   causal_tile     per (head, segment), bf16, d = 64, m <= 256: chunked scan,
+//                   64 tokens per step, projections split by tokens and the
+//                   state by value columns across the four waves
+//   causal_chunk    per (head, segment), every other shape: chunked scan,
+//                   32 tokens per step, state split by features
 // and for the features API:
 //   pack_omega      omega fp32 -> log2(e) omega in operand order
 //   features        phi(x) written to memory
@@ -1382,7 +1386,7 @@ static hipError_t launch_all(const LaunchArgs& a) {
         return hipGetLastError();
     }
     if constexpr (std::is_same<T, bf16>::value && D == 64) {
-        if (a.m == 64 || a.m == 128 || a.m == 256) {
+        if (causal_chunk_tokens(2, D, a.m) == 64) {
             hipError_t err = a.m == 64    ? launch_causal_tile<64>(a, ompack, om_head_vecs, q, k, v, out)
                              : a.m == 128 ? launch_causal_tile<128>(a, ompack, om_head_vecs, q, k, v, out)
                                           : launch_causal_tile<256>(a, ompack, om_head_vecs, q, k, v, out);
@@ -1403,6 +1407,10 @@ static hipError_t launch_all(const LaunchArgs& a) {
     }
     stage_event(a, 3);
     return err;
+}
+
+int causal_chunk_tokens(int dtype_bytes, int D, int m) {
+    return (dtype_bytes == 2 && D == 64 && (m == 64 || m == 128 || m == 256)) ? 64 : 32;
 }
 
 CausalCfg causal_config(int D, int m) {

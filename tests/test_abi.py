@@ -94,10 +94,17 @@ def test_validation(lib, fn):
 
 
 def test_causal_chunk_and_lds_limits(lib):
-    assert _causal(lib, shp(), chunk=64) == UNSUPPORTED
+    # A one-byte workspace makes an accepted shape stop at the workspace
+    # check (WORKSPACE), before anything is launched.
+    # chunk: 0 or the library's length for the shape (64: bf16, d=64, m<=256; else 32)
+    assert _causal(lib, shp(), chunk=64, nbytes=1) == WORKSPACE
+    assert _causal(lib, shp(), chunk=32, nbytes=1) == UNSUPPORTED
+    assert _causal(lib, shp(d=32, m=64), chunk=32, nbytes=1) == WORKSPACE
+    assert _causal(lib, shp(d=32, m=64), chunk=64, nbytes=1) == UNSUPPORTED
+    assert _causal(lib, shp(m=512), chunk=32, nbytes=1) == WORKSPACE
     assert _causal(lib, shp(), chunk=-1) == UNSUPPORTED
     assert _causal(lib, shp(m=96)) == UNSUPPORTED      # causal: m in {32, 64, 128, 256, 512}
-    assert _bidir(lib, shp(m=96), nbytes=1 << 40) != UNSUPPORTED
+    assert _bidir(lib, shp(m=96), nbytes=1) == WORKSPACE
     assert _bidir(lib, shp(d=128, dtype=_lib.FAVOR_F32)) == UNSUPPORTED
     # fp32 d=128 m=512: the causal state does not fit one workgroup's LDS
     assert _causal(lib, shp(d=128, m=512, dtype=_lib.FAVOR_F32)) == UNSUPPORTED
