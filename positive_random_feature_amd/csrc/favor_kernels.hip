@@ -945,18 +945,19 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
 
 // ---------------------------------------------------------------------------
 // causal_tile: chunked causal scan for bf16, d = 64, m <= 256.  One workgroup
-// of four waves per (segment, head); chunks of 64 tokens.  Wave w has two
-// roles in every chunk:
-//   token role   tokens 16w..16w+15 of the chunk: the query and key
-//                projections over all m features (so the per-query shift is
-//                a wave-local maximum), phi(Q) and phi(K) published in LDS,
-//                then the intra-chunk scores S^T[key][query] for keys <= query
-//                and S [V | 1] for its 16 queries;
-//   column role  value columns 16w..16w+15: the state slice G[:, cols]
-//                (all m features, fp32 registers), the inter-chunk term
-//                phi(Q) G for all 64 queries (published in LDS) and the state
-//                update G += phi(K)^T V; also z = sum phi(k) for the feature
-//                blocks kb = w (mod 4), which gives partial denominators.
+// of eight waves per (segment, head); chunks of 64 tokens.  Waves s and s + 4
+// (which share a SIMD) own token tile s (tokens 16s..16s+15 of the chunk) and
+// value-column tile s (columns 16s..16s+15):
+//   query wave s      projects its 16 queries over all m features (the
+//                     per-query shift is a wave-local maximum), publishes
+//                     phi(Q) in LDS, then computes the intra-chunk scores
+//                     S^T[key][query] (keys <= query) and S [V | 1] for its
+//                     queries, and finishes their outputs;
+//   key/state wave s  projects its 16 keys, publishes phi(K) in LDS, holds
+//                     the state slice G[:, 16s..16s+15] (all m features) and
+//                     z for the feature blocks kb = s (mod 4) in fp32
+//                     registers, computes the inter-chunk terms phi(Q) G for
+//                     all 64 queries (published in LDS) and updates G and z.
 // All keys of a segment share one shift (the largest carry-in block shift)
 // and each query one shift over all features, so the contraction over
 // features is exact up to factors that cancel in the ratio (Simple
@@ -984,8 +985,7 @@ struct TileSmem {
 };
 
 template <int M>
-// At most 256 registers: the state stays in VGPRs (no accumulator-register copies).
-__global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, const bf16x8* __restrict__ ompack,
                                                           long long om_head_vecs, const float* __restrict__ carry,
                                                           const float* __restrict__ cmax, bf16* __restrict__ out, int H,
@@ -993,19 +993,21 @@ __global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restr
     using SM = TileSmem<M>;
     constexpr int D = SM::D, KSD = SM::KSD, NFB = SM::NFB, NFT = SM::NFT, RS = SM::RS, PKS = SM::PKS, OS = SM::OS;
     constexpr int D1 = D + 1;
-    constexpr int ZB = (NFB + 3) / 4;  // z blocks per wave (kb = w + 4 zb)
+    constexpr int ZB = (NFB + 3) / 4;  // z blocks per state wave (kb = s + 4 zb)
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     bf16x8* om = reinterpret_cast<bf16x8*>(smem_raw + SM::OFF_OM);
     bf16* tq = reinterpret_cast<bf16*>(smem_raw + SM::OFF_TQ);
     bf16* tk = reinterpret_cast<bf16*>(smem_raw + SM::OFF_TK);
     bf16* tv0 = reinterpret_cast<bf16*>(smem_raw + SM::OFF_TV);
-    float* nrm = reinterpret_cast<float*>(smem_raw + SM::OFF_NRM);  // [half][K rows | Q rows]
+    float* nrm = reinterpret_cast<float*>(smem_raw + SM::OFF_NRM);  // [K rows 0..63 | Q rows 0..63]
     bf16x8* phq = reinterpret_cast<bf16x8*>(smem_raw + SM::OFF_PQ);
     bf16* phk = reinterpret_cast<bf16*>(smem_raw + SM::OFF_PK);
     float* oin = reinterpret_cast<float*>(smem_raw + SM::OFF_OI);
     float* dpart = reinterpret_cast<float*>(smem_raw + SM::OFF_DP);
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
+    const int s = w & 3;            // token tile and value-column tile of this wave
+    const bool qwave = w < 4;       // query wave (else key/state wave)
     const int seg = blockIdx.x, bh = blockIdx.y, h = bh % H;
     const int t_begin = seg * seg_len;
     const int t_end = min(L, t_begin + seg_len);
@@ -1014,35 +1016,35 @@ __global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restr
     const bf16* src[3] = {k + xbase, q + xbase, v + xbase};
 
     // chunk 0 into registers
-    Prefetch<bf16, D, 256, 3> pf[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) pf[hf].load(src, t_begin + 32 * hf, L - 1);
+    Prefetch<bf16, D, 512, 3, 64> pf;
+    pf.load(src, t_begin, L - 1);
 
     // projection operands of this head into LDS
     {
         const bf16x8* omh = ompack + (size_t)(om_head_vecs ? h : 0) * (size_t)om_head_vecs;
-        copy_to_lds<256>(om, omh, NFT * KSD * 64);
+        copy_to_lds<512>(om, omh, NFT * KSD * 64);
     }
 
-    // carry-in: state slice for columns 16w.. and z for this wave's blocks,
-    // rescaled from the per-block shifts to the segment's common key shift
+    // carry-in (state waves): state slice for columns 16s.. and z for this
+    // wave's blocks, rescaled from the per-block shifts to the segment's
+    // common key shift
     const float* cm = cmax + ((size_t)bh * nseg + seg) * NFB;
     float Mseg = kNegInf;
 #pragma unroll
     for (int b = 0; b < NFB; ++b) Mseg = __builtin_fmaxf(Mseg, cm[b]);
     f4 G[NFT];
     f4 Z[2 * ZB];
-    {
+    if (!qwave) {
         const float* cb = carry + ((size_t)bh * nseg + seg) * (size_t)M * D1;
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft) {
             const float mb = cm[ft / 2];
             const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
-            G[ft] = sc * *reinterpret_cast<const f4*>(cb + seg_v_off<D>(ft, w, lane));
+            G[ft] = sc * *reinterpret_cast<const f4*>(cb + seg_v_off<D>(ft, s, lane));
         }
 #pragma unroll
         for (int zb = 0; zb < ZB; ++zb) {
-            const int kb = w + 4 * zb;
+            const int kb = s + 4 * zb;
             const bool own = kb < NFB;
             const float mb = own ? cm[kb] : kNegInf;
             const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
@@ -1057,34 +1059,26 @@ __global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restr
         // past the last chunk: rows of the last chunk, zeroed, into the V
         // buffer the last chunk does not use
         const int cc = min(ci, nch - 1);
-        bf16* tv = tv0 + (size_t)(ci & 1) * SM::TILE;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            bf16* dst[3] = {tk + 32 * hf * RS, tq + 32 * hf * RS, tv + 32 * hf * RS};
-            pf[hf].template store<true>(dst, nrm + 64 * hf, 3, t_begin + 64 * cc + 32 * hf, ci < nch ? t_end : -1);
-        }
+        bf16* dst[3] = {tk, tq, tv0 + (size_t)(ci & 1) * SM::TILE};
+        pf.template store<true>(dst, nrm, 3, t_begin + 64 * cc, ci < nch ? t_end : -1);
     };
-    auto prefetch_chunk = [&](int ci) {
-        const int cc = min(ci, nch - 1);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) pf[hf].load(src, t_begin + 64 * cc + 32 * hf, L - 1);
-    };
+    auto prefetch_chunk = [&](int ci) { pf.load(src, t_begin + 64 * min(ci, nch - 1), L - 1); };
 
     stage_chunk(0);
     prefetch_chunk(1);
     __syncthreads();
 
     const bf16x8 ones = splat8<bf16>(1.0f);
-    f4 oi[5];  // intra-chunk terms of this wave's 16 queries: 4 column tiles, denominator
+    f4 oi[5];  // query waves: intra-chunk terms of the 16 queries (4 column tiles, denominator)
     // lane offsets into the swizzled arrays (everything else is a constant)
     const int off_trv = kappa_lane_off(lane, swz_tile);       // V, transpose reads
     const int off_trk = kappa_lane_off(lane, swz_rows<PKS>);  // phi(K), transpose reads
-    const int off_row = swz_tile(r, 8 * g);                   // Q/K rows 16w + r
+    const int off_row = swz_tile(r, 8 * g);                   // Q/K rows 16s + r
     const int off_krow = swz_rows<PKS>(r, 4 * g);             // phi(K) rows 16 kt + r
 
-    // outputs of chunk cc for tokens 16w..16w+15
+    // outputs of chunk cc for tokens 16s..16s+15 (query waves)
     auto finalize = [&](int cc) {
-        const int row = 16 * w + r;
+        const int row = 16 * s + r;
         const int t = t_begin + 64 * cc + row;
         float den = oi[4][0];
 #pragma unroll
@@ -1100,35 +1094,22 @@ __global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restr
     for (int c = 0; c < nch; ++c) {
         const int t0 = t_begin + 64 * c;
         const bf16* tv = tv0 + (size_t)(c & 1) * SM::TILE;
-        if (c > 0) finalize(c - 1);
-
-        // ---- token role: projections of tokens 16w..16w+15
+        const int row = 16 * s + r;
         bf16x8 bq[NFB];
-        {
-            const int row = 16 * w + r;
-            const float* nh = nrm + 64 * (row >> 5);
-            const float ck = (t0 + row < t_end) ? nh[row & 31] - Mseg : kNegInf;
-            const float cq = nh[32 + (row & 31)];
-            bf16x8 xk[KSD], xq[KSD];
+        if (qwave) {
+            if (c > 0) finalize(c - 1);
+            // ---- queries 16s..16s+15: projection, per-query shift, phi(Q)
+            const float cq = nrm[64 + row];
+            bf16x8 xq[KSD];
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                xk[ks] = *reinterpret_cast<const bf16x8*>(tk + off_row + 16 * w * RS + 32 * ks);
-                xq[ks] = *reinterpret_cast<const bf16x8*>(tq + off_row + 16 * w * RS + 32 * ks);
-            }
+            for (int ks = 0; ks < KSD; ++ks)
+                xq[ks] = *reinterpret_cast<const bf16x8*>(tq + off_row + 16 * s * RS + 32 * ks);
             f4 pq[NFT];
 #pragma unroll
             for (int ft = 0; ft < NFT; ++ft) {
-                f4 pk = f4splat(ck);
                 pq[ft] = f4splat(cq);
 #pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) {
-                    const bf16x8 a = om[(ft * KSD + ks) * 64 + lane];
-                    pk = mma32(a, xk[ks], pk);
-                    pq[ft] = mma32(a, xq[ks], pq[ft]);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pk[i] = exp2f_fast(pk[i]);
-                lds_store4(phk + off_krow + 16 * w * PKS + 16 * ft, pk);
+                for (int ks = 0; ks < KSD; ++ks) pq[ft] = mma32(om[(ft * KSD + ks) * 64 + lane], xq[ks], pq[ft]);
             }
             float mx = kNegInf;
 #pragma unroll
@@ -1145,7 +1126,23 @@ __global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restr
                     e1[i] = exp2f_fast(pq[2 * kb + 1][i] - mx);
                 }
                 bq[kb] = pack8t<bf16>(e0, e1);
-                phq[(w * NFB + kb) * 64 + lane] = bq[kb];
+                phq[(s * NFB + kb) * 64 + lane] = bq[kb];
+            }
+        } else {
+            // ---- keys 16s..16s+15: projection with the segment's shift, phi(K)
+            const float ck = (t0 + row < t_end) ? nrm[row] - Mseg : kNegInf;
+            bf16x8 xk[KSD];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks)
+                xk[ks] = *reinterpret_cast<const bf16x8*>(tk + off_row + 16 * s * RS + 32 * ks);
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) {
+                f4 pk = f4splat(ck);
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) pk = mma32(om[(ft * KSD + ks) * 64 + lane], xk[ks], pk);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk[i] = exp2f_fast(pk[i]);
+                lds_store4(phk + off_krow + 16 * s * PKS + 16 * ft, pk);
             }
         }
         __syncthreads();
@@ -1154,39 +1151,43 @@ __global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restr
         stage_chunk(c + 1);
         prefetch_chunk(c + 2);
 
-        // ---- token role: intra-chunk terms for queries 16w..16w+15
-        {
-            // every wave runs the full 64 x 64 block (the last wave needs all
-            // of it, so this costs no time) and zeroes keys after the query
+        if (qwave) {
+            // ---- intra-chunk terms for queries 16s..16s+15: key tiles
+            // 0..s (later ones are all masked), keys after the query zeroed
             f4 st[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
                 st[kt] = f4splat(0.0f);
-                const bf16* pr = phk + off_krow + 16 * kt * PKS;
+                if (kt <= s) {
+                    const bf16* pr = phk + off_krow + 16 * kt * PKS;
 #pragma unroll
-                for (int kb = 0; kb < NFB; ++kb) {
-                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(pr + 32 * kb);
-                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(pr + 32 * kb + 16);
-                    const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    st[kt] = mma32(a, bq[kb], st[kt]);
+                    for (int kb = 0; kb < NFB; ++kb) {
+                        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(pr + 32 * kb);
+                        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(pr + 32 * kb + 16);
+                        const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        st[kt] = mma32(a, bq[kb], st[kt]);
+                    }
+                    if (kt == s) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (4 * g + i > r) st[kt][i] = 0.0f;
+                    }
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (16 * kt + 4 * g + i > 16 * w + r) st[kt][i] = 0.0f;
             }
 #pragma unroll
             for (int ct = 0; ct < 5; ++ct) oi[ct] = f4splat(0.0f);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const bf16x8 b = pack8t<bf16>(st[2 * j], st[2 * j + 1]);
+                if (2 * j <= s) {
+                    const bf16x8 b = pack8t<bf16>(st[2 * j], st[2 * j + 1]);
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) oi[ct] = mma32(kappa_col_at<RS>(tv + off_trv + 32 * j * RS + 16 * ct), b, oi[ct]);
-                oi[4] = mma32(ones, b, oi[4]);
+                    for (int ct = 0; ct < 4; ++ct)
+                        oi[ct] = mma32(kappa_col_at<RS>(tv + off_trv + 32 * j * RS + 16 * ct), b, oi[ct]);
+                    oi[4] = mma32(ones, b, oi[4]);
+                }
             }
-        }
-
-        // ---- column role: inter-chunk terms phi(Q) G for all 64 queries
-        {
+        } else {
+            // ---- inter-chunk terms phi(Q) G for all 64 queries
             bf16x8 ga[NFB];
 #pragma unroll
             for (int kb = 0; kb < NFB; ++kb) ga[kb] = pack8t<bf16>(G[2 * kb], G[2 * kb + 1]);
@@ -1198,32 +1199,31 @@ __global__ __launch_bounds__(256, 2) void causal_tile_kernel(const bf16* __restr
                 f4 o = f4splat(0.0f);
 #pragma unroll
                 for (int kb = 0; kb < NFB; ++kb) o = mma32(ga[kb], phq[(qt * NFB + kb) * 64 + lane], o);
-                *reinterpret_cast<f4*>(oin + (16 * qt + r) * OS + 16 * w + 4 * g) = o;
+                *reinterpret_cast<f4*>(oin + (16 * qt + r) * OS + 16 * s + 4 * g) = o;
                 // z blocks past m are zero (their index is clamped for the read)
                 f4 dz = f4splat(0.0f);
 #pragma unroll
                 for (int zb = 0; zb < ZB; ++zb)
-                    dz = mma32(za[zb], phq[(qt * NFB + min(w + 4 * zb, NFB - 1)) * 64 + lane], dz);
-                if (g == 0 && w < NFB) dpart[w * 64 + 16 * qt + r] = dz[0];
+                    dz = mma32(za[zb], phq[(qt * NFB + min(s + 4 * zb, NFB - 1)) * 64 + lane], dz);
+                if (g == 0 && s < NFB) dpart[s * 64 + 16 * qt + r] = dz[0];
             }
-        }
-
-        // ---- column role: state update G += phi(K)^T V, z += phi(K)^T 1
+            // ---- state update G += phi(K)^T V, z += phi(K)^T 1
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const bf16* pj = phk + off_trk + 32 * j * PKS;
-            const bf16x8 bv = kappa_col_at<RS>(tv + off_trv + 32 * j * RS + 16 * w);
+            for (int j = 0; j < 2; ++j) {
+                const bf16* pj = phk + off_trk + 32 * j * PKS;
+                const bf16x8 bv = kappa_col_at<RS>(tv + off_trv + 32 * j * RS + 16 * s);
 #pragma unroll
-            for (int ft = 0; ft < NFT; ++ft) G[ft] = mma32(kappa_col_at<PKS>(pj + 16 * ft), bv, G[ft]);
+                for (int ft = 0; ft < NFT; ++ft) G[ft] = mma32(kappa_col_at<PKS>(pj + 16 * ft), bv, G[ft]);
 #pragma unroll
-            for (int zt = 0; zt < 2 * ZB; ++zt) {
-                const int ft = min(2 * (w + 4 * (zt / 2)) + (zt % 2), NFT - 1);
-                Z[zt] = mma32(kappa_col_at<PKS>(pj + 16 * ft), ones, Z[zt]);
+                for (int zt = 0; zt < 2 * ZB; ++zt) {
+                    const int ft = min(2 * (s + 4 * (zt / 2)) + (zt % 2), NFT - 1);
+                    Z[zt] = mma32(kappa_col_at<PKS>(pj + 16 * ft), ones, Z[zt]);
+                }
             }
         }
         __syncthreads();
     }
-    finalize(nch - 1);
+    if (qwave) finalize(nch - 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1320,7 +1320,7 @@ static hipError_t launch_causal_tile(const LaunchArgs& a, const bf16x8* ompack, 
     static_assert(bytes <= kMaxLds, "causal_tile LDS");
     auto kern = causal_tile_kernel<M>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H), dim3(256), bytes, a.stream, q, k, v, ompack, om_head_vecs,
+    hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H), dim3(512), bytes, a.stream, q, k, v, ompack, om_head_vecs,
                        a.ws_carry, a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
     return hipGetLastError();
 }
