@@ -1135,14 +1135,20 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks)
                 xk[ks] = *reinterpret_cast<const bf16x8*>(tk + off_row + 16 * s * RS + 32 * ks);
+            // all projections first (independent accumulators), then the
+            // exponentials and stores
+            f4 pk[NFT];
 #pragma unroll
             for (int ft = 0; ft < NFT; ++ft) {
-                f4 pk = f4splat(ck);
+                pk[ft] = f4splat(ck);
 #pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) pk = mma32(om[(ft * KSD + ks) * 64 + lane], xk[ks], pk);
+                for (int ks = 0; ks < KSD; ++ks) pk[ft] = mma32(om[(ft * KSD + ks) * 64 + lane], xk[ks], pk[ft]);
+            }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pk[i] = exp2f_fast(pk[i]);
-                lds_store4(phk + off_krow + 16 * s * PKS + 16 * ft, pk);
+            for (int ft = 0; ft < NFT; ++ft) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk[ft][i] = exp2f_fast(pk[ft][i]);
+                lds_store4(phk + off_krow + 16 * s * PKS + 16 * ft, pk[ft]);
             }
         }
         __syncthreads();
