@@ -1069,110 +1069,91 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
     __syncthreads();
 
     const bf16x8 ones = splat8<bf16>(1.0f);
-    f4 oi[5];  // query waves: intra-chunk terms of the 16 queries (4 column tiles, denominator)
     // lane offsets into the swizzled arrays (everything else is a constant)
     const int off_trv = kappa_lane_off(lane, swz_tile);       // V, transpose reads
     const int off_trk = kappa_lane_off(lane, swz_rows<PKS>);  // phi(K), transpose reads
-    const int off_row = swz_tile(r, 8 * g);                   // Q/K rows 16s + r
+    const int off_row = swz_tile(r, 8 * g);                   // Q/K rows 16 tt + r
     const int off_krow = swz_rows<PKS>(r, 4 * g);             // phi(K) rows 16 kt + r
 
-    // outputs of chunk cc for tokens 16s..16s+15 (query waves)
-    auto finalize = [&](int cc) {
-        const int row = 16 * s + r;
-        const int t = t_begin + 64 * cc + row;
-        float den = oi[4][0];
+    // The two roles run separate loops (so each keeps only its own registers
+    // live) with the same barriers in the same order.
+    if (qwave) {
+        f4 oi[5];  // intra-chunk terms of the 16 queries: 4 column tiles, denominator
+        // outputs of chunk cc for tokens 16s..16s+15
+        auto finalize = [&](int cc) {
+            const int row = 16 * s + r;
+            const int t = t_begin + 64 * cc + row;
+            float den = oi[4][0];
 #pragma unroll
-        for (int c = 0; c < (NFB < 4 ? NFB : 4); ++c) den += dpart[c * 64 + row];
-        const float inv = __builtin_amdgcn_rcpf(den);
+            for (int c = 0; c < (NFB < 4 ? NFB : 4); ++c) den += dpart[c * 64 + row];
+            const float inv = __builtin_amdgcn_rcpf(den);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const f4 o = *reinterpret_cast<const f4*>(oin + row * OS + 16 * ct + 4 * g) + oi[ct];
-            if (t < t_end) store4(out + xbase + (size_t)t * D + 16 * ct + 4 * g, o * inv);
-        }
-    };
-
-    for (int c = 0; c < nch; ++c) {
-        const int t0 = t_begin + 64 * c;
-        const bf16* tv = tv0 + (size_t)(c & 1) * SM::TILE;
-        const int row = 16 * s + r;
-        bf16x8 bq[NFB];
-        if (qwave) {
+            for (int ct = 0; ct < 4; ++ct) {
+                const f4 o = *reinterpret_cast<const f4*>(oin + row * OS + 16 * ct + 4 * g) + oi[ct];
+                if (t < t_end) store4(out + xbase + (size_t)t * D + 16 * ct + 4 * g, o * inv);
+            }
+        };
+        for (int c = 0; c < nch; ++c) {
+            const bf16* tv = tv0 + (size_t)(c & 1) * SM::TILE;
             if (c > 0) finalize(c - 1);
             // ---- queries 16s..16s+15: projection, per-query shift, phi(Q)
-            const float cq = nrm[64 + row];
-            bf16x8 xq[KSD];
+            bf16x8 bq[NFB];
+            {
+                const float cq = nrm[64 + 16 * s + r];
+                bf16x8 xq[KSD];
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks)
-                xq[ks] = *reinterpret_cast<const bf16x8*>(tq + off_row + 16 * s * RS + 32 * ks);
-            f4 pq[NFT];
+                for (int ks = 0; ks < KSD; ++ks)
+                    xq[ks] = *reinterpret_cast<const bf16x8*>(tq + off_row + 16 * s * RS + 32 * ks);
+                f4 pq[NFT];
 #pragma unroll
-            for (int ft = 0; ft < NFT; ++ft) {
-                pq[ft] = f4splat(cq);
+                for (int ft = 0; ft < NFT; ++ft) {
+                    pq[ft] = f4splat(cq);
 #pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) pq[ft] = mma32(om[(ft * KSD + ks) * 64 + lane], xq[ks], pq[ft]);
-            }
-            float mx = kNegInf;
-#pragma unroll
-            for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[ft][i]);
-            mx = col_max(mx);
-#pragma unroll
-            for (int kb = 0; kb < NFB; ++kb) {
-                f4 e0, e1;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    e0[i] = exp2f_fast(pq[2 * kb][i] - mx);
-                    e1[i] = exp2f_fast(pq[2 * kb + 1][i] - mx);
+                    for (int ks = 0; ks < KSD; ++ks) pq[ft] = mma32(om[(ft * KSD + ks) * 64 + lane], xq[ks], pq[ft]);
                 }
-                bq[kb] = pack8t<bf16>(e0, e1);
-                phq[(s * NFB + kb) * 64 + lane] = bq[kb];
+                float mx = kNegInf;
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[ft][i]);
+                mx = col_max(mx);
+#pragma unroll
+                for (int kb = 0; kb < NFB; ++kb) {
+                    f4 e0, e1;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        e0[i] = exp2f_fast(pq[2 * kb][i] - mx);
+                        e1[i] = exp2f_fast(pq[2 * kb + 1][i] - mx);
+                    }
+                    bq[kb] = pack8t<bf16>(e0, e1);
+                    phq[(s * NFB + kb) * 64 + lane] = bq[kb];
+                }
             }
-        } else {
-            // ---- keys 16s..16s+15: projection with the segment's shift, phi(K)
-            const float ck = (t0 + row < t_end) ? nrm[row] - Mseg : kNegInf;
-            bf16x8 xk[KSD];
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks)
-                xk[ks] = *reinterpret_cast<const bf16x8*>(tk + off_row + 16 * s * RS + 32 * ks);
-            // all projections first (independent accumulators), then the
-            // exponentials and stores
-            f4 pk[NFT];
-#pragma unroll
-            for (int ft = 0; ft < NFT; ++ft) {
-                pk[ft] = f4splat(ck);
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) pk[ft] = mma32(om[(ft * KSD + ks) * 64 + lane], xk[ks], pk[ft]);
-            }
-#pragma unroll
-            for (int ft = 0; ft < NFT; ++ft) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pk[ft][i] = exp2f_fast(pk[ft][i]);
-                lds_store4(phk + off_krow + 16 * s * PKS + 16 * ft, pk[ft]);
-            }
-        }
-        __syncthreads();
+            __syncthreads();
 
-        // next chunk's tiles (Q, K and this V buffer's partner are free now)
-        stage_chunk(c + 1);
-        prefetch_chunk(c + 2);
+            // next chunk's tiles (Q, K and this V buffer's partner are free now)
+            stage_chunk(c + 1);
+            prefetch_chunk(c + 2);
 
-        if (qwave) {
-            // ---- intra-chunk terms for queries 16s..16s+15: key tiles
-            // 0..s (later ones are all masked), keys after the query zeroed
+            // ---- intra-chunk terms for queries 16s..16s+15: key tiles 0..s
+            // (later ones are all masked), keys after the query zeroed
             f4 st[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
                 st[kt] = f4splat(0.0f);
                 if (kt <= s) {
+                    // all operand reads of the tile first, then the products
                     const bf16* pr = phk + off_krow + 16 * kt * PKS;
+                    bf16x8 a[NFB];
 #pragma unroll
                     for (int kb = 0; kb < NFB; ++kb) {
                         const bf16x4 lo = *reinterpret_cast<const bf16x4*>(pr + 32 * kb);
                         const bf16x4 hi = *reinterpret_cast<const bf16x4*>(pr + 32 * kb + 16);
-                        const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        st[kt] = mma32(a, bq[kb], st[kt]);
+                        a[kb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     }
+                    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+                    for (int kb = 0; kb < NFB; ++kb) st[kt] = mma32(a[kb], bq[kb], st[kt]);
                     if (kt == s) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
@@ -1192,26 +1173,80 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
                     oi[4] = mma32(ones, b, oi[4]);
                 }
             }
-        } else {
+            __syncthreads();
+        }
+        finalize(nch - 1);
+    } else {
+        // key/state wave: feature tiles ft = s + 4 f of the key projection
+        // (their projection operands stay in registers), the state slice for
+        // value columns 16s.. and z for feature blocks kb = s + 4 zb
+        constexpr int KFT = (NFT + 3) / 4;
+        vec8<bf16> omr[KFT][KSD];
+#pragma unroll
+        for (int f = 0; f < KFT; ++f)
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) omr[f][ks] = om[((s + 4 * f) * KSD + ks) * 64 + lane];
+        for (int c = 0; c < nch; ++c) {
+            const int t0 = t_begin + 64 * c;
+            const bf16* tv = tv0 + (size_t)(c & 1) * SM::TILE;
+            // ---- keys of the chunk, this wave's feature tiles, the segment's shift
+            {
+                f4 pk[4][KFT];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int row = 16 * tt + r;
+                    const float ck = (t0 + row < t_end) ? nrm[row] - Mseg : kNegInf;
+                    bf16x8 xk[KSD];
+#pragma unroll
+                    for (int ks = 0; ks < KSD; ++ks)
+                        xk[ks] = *reinterpret_cast<const bf16x8*>(tk + off_row + 16 * tt * RS + 32 * ks);
+#pragma unroll
+                    for (int f = 0; f < KFT; ++f) {
+                        pk[tt][f] = f4splat(ck);
+#pragma unroll
+                        for (int ks = 0; ks < KSD; ++ks) pk[tt][f] = mma32(omr[f][ks], xk[ks], pk[tt][f]);
+                    }
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int f = 0; f < KFT; ++f) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pk[tt][f][i] = exp2f_fast(pk[tt][f][i]);
+                        lds_store4(phk + off_krow + 16 * tt * PKS + 16 * (s + 4 * f), pk[tt][f]);
+                    }
+            }
+            __syncthreads();
+
+            stage_chunk(c + 1);
+            prefetch_chunk(c + 2);
+
             // ---- inter-chunk terms phi(Q) G for all 64 queries
-            bf16x8 ga[NFB];
+            {
+                bf16x8 ga[NFB];
 #pragma unroll
-            for (int kb = 0; kb < NFB; ++kb) ga[kb] = pack8t<bf16>(G[2 * kb], G[2 * kb + 1]);
-            bf16x8 za[ZB];
+                for (int kb = 0; kb < NFB; ++kb) ga[kb] = pack8t<bf16>(G[2 * kb], G[2 * kb + 1]);
+                bf16x8 za[ZB];
 #pragma unroll
-            for (int zb = 0; zb < ZB; ++zb) za[zb] = pack8t<bf16>(Z[2 * zb], Z[2 * zb + 1]);
+                for (int zb = 0; zb < ZB; ++zb) za[zb] = pack8t<bf16>(Z[2 * zb], Z[2 * zb + 1]);
 #pragma unroll
-            for (int qt = 0; qt < 4; ++qt) {
-                f4 o = f4splat(0.0f);
+                for (int qt = 0; qt < 4; ++qt) {
+                    // all operand reads of the query tile first, then the products
+                    bf16x8 b[NFB];
 #pragma unroll
-                for (int kb = 0; kb < NFB; ++kb) o = mma32(ga[kb], phq[(qt * NFB + kb) * 64 + lane], o);
-                *reinterpret_cast<f4*>(oin + (16 * qt + r) * OS + 16 * s + 4 * g) = o;
-                // z blocks past m are zero (their index is clamped for the read)
-                f4 dz = f4splat(0.0f);
+                    for (int kb = 0; kb < NFB; ++kb) b[kb] = phq[(qt * NFB + kb) * 64 + lane];
+                    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+                    f4 o = f4splat(0.0f);
 #pragma unroll
-                for (int zb = 0; zb < ZB; ++zb)
-                    dz = mma32(za[zb], phq[(qt * NFB + min(s + 4 * zb, NFB - 1)) * 64 + lane], dz);
-                if (g == 0 && s < NFB) dpart[s * 64 + 16 * qt + r] = dz[0];
+                    for (int kb = 0; kb < NFB; ++kb) o = mma32(ga[kb], b[kb], o);
+                    *reinterpret_cast<f4*>(oin + (16 * qt + r) * OS + 16 * s + 4 * g) = o;
+                    // z blocks past m are zero (their index is clamped for the read)
+                    f4 dz = f4splat(0.0f);
+#pragma unroll
+                    for (int zb = 0; zb < ZB; ++zb)
+                        dz = mma32(za[zb], phq[(qt * NFB + min(s + 4 * zb, NFB - 1)) * 64 + lane], dz);
+                    if (g == 0 && s < NFB) dpart[s * 64 + 16 * qt + r] = dz[0];
+                }
             }
             // ---- state update G += phi(K)^T V, z += phi(K)^T 1
 #pragma unroll
@@ -1226,10 +1261,9 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
                     Z[zt] = mma32(kappa_col_at<PKS>(pj + 16 * ft), ones, Z[zt]);
                 }
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
-    if (qwave) finalize(nch - 1);
 }
 
 // ---------------------------------------------------------------------------
