@@ -222,9 +222,8 @@ __device__ __forceinline__ size_t seg_v_off(int ft, int nt, int lane) {
 // kv_partial: one workgroup (8 waves) per (segment, head, group of <= 256
 // features).  Wave w owns 32 features.  Steps of 64 tokens are prefetched PD
 // ahead into registers and staged into one of three LDS slots (one barrier
-// per step).  The loop is software-pipelined: while step i's features are
-// exponentiated and accumulated, step i+1's projection is already issued, so
-// matrix-core and vector work of one wave overlap.
+// per step).  The loop is software-pipelined: step i's exponentials, step
+// i+1's projection and step i's update are independent and interleave.
 // Projection D[T x F] = K Omega'^T with the accumulator initialised to
 // -log2(e)|k|^2/2 - M: values are relative to the wave's shift M, which is
 // set from the first step's maximum and afterwards raised lazily (a
@@ -343,31 +342,13 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
             stage(pf[(u + 1) % PD], it + 1);
             __syncthreads();
             if (active && it < nsteps) {
-                // next step's projection first (independent of this step's update)
-                f4 pn[4][NFT];
-                if (it + 1 < nsteps) {
-                    const float lm = project(it + 1, pn);
-                    if (wave_any(lm > kTau)) {
-                        const float tm = wave_max_uniform(lm);  // raise M by tm
-                        const float sc = exp2f_fast(-tm);
+                // this step's features (exponentials of values already relative
+                // to M), the next step's projection and this step's update are
+                // independent and interleave; the shift test for the next step
+                // comes last, so a raise rescales sums that include this step
+                vec8<T> a[2][NFT];
 #pragma unroll
-                        for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-                            for (int nt = 0; nt < NT; ++nt) kv[ft][nt] *= sc;
-#pragma unroll
-                        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                            for (int ft = 0; ft < NFT; ++ft) {
-                                pc[tt][ft] -= tm;
-                                pn[tt][ft] -= tm;
-                            }
-                        M += tm;
-                    }
-                }
-                const T* vt = tiles[it % 3][1];
-#pragma unroll
-                for (int ks2 = 0; ks2 < 2; ++ks2) {  // tokens 32 ks2 .. 32 ks2 + 31
-                    vec8<T> a[NFT];
+                for (int ks2 = 0; ks2 < 2; ++ks2)  // tokens 32 ks2 .. 32 ks2 + 31
 #pragma unroll
                     for (int ft = 0; ft < NFT; ++ft) {
                         f4 e0, e1;
@@ -376,18 +357,38 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
                             e0[i] = exp2f_fast(pc[2 * ks2][ft][i]);
                             e1[i] = exp2f_fast(pc[2 * ks2 + 1][ft][i]);
                         }
-                        a[ft] = pack8t<T>(e0, e1);
+                        a[ks2][ft] = pack8t<T>(e0, e1);
                     }
+                f4 pn[4][NFT];
+                float lm = kNegInf;
+                const bool more = it + 1 < nsteps;
+                if (more) lm = project(it + 1, pn);
+                const T* vt = tiles[it % 3][1];
+#pragma unroll
+                for (int ks2 = 0; ks2 < 2; ++ks2) {
                     const T* vk = vt + 32 * ks2 * RS;
 #pragma unroll
                     for (int nt = 0; nt < NT - 1; ++nt) {
                         const vec8<T> vb = kappa_col<RS>(vk, 16 * nt, lane);
 #pragma unroll
-                        for (int ft = 0; ft < NFT; ++ft) kv[ft][nt] = mma32(a[ft], vb, kv[ft][nt]);
+                        for (int ft = 0; ft < NFT; ++ft) kv[ft][nt] = mma32(a[ks2][ft], vb, kv[ft][nt]);
                     }
                     const vec8<T> ones = splat8<T>(1.0f);
 #pragma unroll
-                    for (int ft = 0; ft < NFT; ++ft) kv[ft][NT - 1] = mma32(a[ft], ones, kv[ft][NT - 1]);
+                    for (int ft = 0; ft < NFT; ++ft) kv[ft][NT - 1] = mma32(a[ks2][ft], ones, kv[ft][NT - 1]);
+                }
+                if (more && wave_any(lm > kTau)) {
+                    const float tm = wave_max_uniform(lm);  // raise M by tm
+                    const float sc = exp2f_fast(-tm);
+#pragma unroll
+                    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) kv[ft][nt] *= sc;
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                        for (int ft = 0; ft < NFT; ++ft) pn[tt][ft] -= tm;
+                    M += tm;
                 }
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
