@@ -577,9 +577,11 @@ __global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q,
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) acc[mt][tt] = f4splat(0.0f);
+    // per-query shift (log2 units), folded into the projection's
+    // initialisation: every projected value is already relative to it
     float sref[NTT];
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) sref[tt] = kNegInf;
+    for (int tt = 0; tt < NTT; ++tt) sref[tt] = 0.0f;
 
     // projection of one 32-feature chunk for all query tiles; the next
     // chunk's projection is issued before the current chunk's exponentials
@@ -589,7 +591,7 @@ __global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q,
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) pp[tt][hh] = f4splat(cq[tt] + off);
+            for (int hh = 0; hh < 2; ++hh) pp[tt][hh] = f4splat(cq[tt] + off - sref[tt]);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -601,6 +603,18 @@ __global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q,
     };
     f4 pn[NTT][2];
     project(0, pn);
+    // the first chunk sets each query's shift to its maximum
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+        float lm = kNegInf;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lm = __builtin_fmaxf(lm, pn[tt][hh][i]);
+        sref[tt] = col_max(lm);
+        pn[tt][0] -= sref[tt];
+        pn[tt][1] -= sref[tt];
+    }
     for (int fb = 0; fb < nfb; ++fb) {
         f4 p[NTT][2];
 #pragma unroll
@@ -608,7 +622,8 @@ __global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q,
             p[tt][0] = pn[tt][0];
             p[tt][1] = pn[tt][1];
         }
-        if (fb + 1 < nfb) project(fb + 1, pn);
+        const bool more = fb + 1 < nfb;
+        if (more) project(fb + 1, pn);
         float lm[NTT];
         bool need = false;
 #pragma unroll
@@ -618,17 +633,25 @@ __global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q,
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) lm[tt] = __builtin_fmaxf(lm[tt], p[tt][hh][i]);
-            need |= lm[tt] > sref[tt] + kTau;
+            need |= lm[tt] > kTau;
         }
         if (wave_any(need)) {
+            // raise the shift of the queries that need it, rescaling their sums
+            // and the values already projected with the old shift
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
                 const float cm = col_max(lm[tt]);
-                if (cm > sref[tt] + kTau) {
-                    const float sc = (sref[tt] == kNegInf) ? 0.0f : exp2f_fast(sref[tt] - cm);
+                const float up = cm > kTau ? cm : 0.0f;
+                if (cm > kTau) {
+                    const float sc = exp2f_fast(-cm);
 #pragma unroll
                     for (int mt = 0; mt < NMT; ++mt) acc[mt][tt] *= sc;
-                    sref[tt] = cm;
+                }
+                sref[tt] += up;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    p[tt][hh] -= up;
+                    pn[tt][hh] -= up;
                 }
             }
         }
@@ -638,8 +661,8 @@ __global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q,
             f4 e0, e1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                e0[i] = exp2f_fast(p[tt][0][i] - sref[tt]);
-                e1[i] = exp2f_fast(p[tt][1][i] - sref[tt]);
+                e0[i] = exp2f_fast(p[tt][0][i]);
+                e1[i] = exp2f_fast(p[tt][1][i]);
             }
             bq[tt] = pack8t<T>(e0, e1);
         }
