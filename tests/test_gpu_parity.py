@@ -140,6 +140,19 @@ def test_workload_causal_64k_sampled():
 # invariances and edge cases
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("d,m", [(64, 256), (64, 128), (32, 64), (128, 128)])
+@pytest.mark.parametrize("B,H,L", [(2, 8, 2000), (1, 16, 1411)])
+def test_causal_ragged_segments(d, m, B, H, L):
+    """Segments of several chunks with a ragged last segment and a partial
+    last chunk (B*H = 16: 16 segments of 128 or 64+ tokens), every element."""
+    w = WORKLOADS["causal_bf16_8k"].replace(d=d, m=m)
+    inp, om, got = _run(w, "causal", B, H, L)
+    want = native.causal(inp.q, inp.k, inp.v, om)
+    err = _rel(got, want)
+    _log(f"causal ragged segments d={d} m={m} {B}x{H}x{L}", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
 def test_causal_prefix_invariance():
     """Causal outputs of a prefix do not depend on later tokens, whatever the
     segmentation chosen for the two lengths."""
