@@ -25,8 +25,9 @@
 //                   also packs log2(e) omega in operand order
 //   bidir_out       phi(q) . [KV | z] for tiles of 32 queries per wave
 //   causal_tile     per (head, segment), bf16, d = 64, m <= 256: chunked scan,
-//                   64 tokens per step, projections split by tokens and the
-//                   state by value columns across the four waves
+//                   64 tokens per step; four query waves (one 16-query tile
+//                   each) and four key/state waves (key projection by
+//                   feature slice, state by value columns)
 //   causal_chunk    per (head, segment), every other shape: chunked scan,
 //                   32 tokens per step, state split by features
 // and for the features API:
@@ -977,8 +978,10 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
 //                     phi(Q) in LDS, then computes the intra-chunk scores
 //                     S^T[key][query] (keys <= query) and S [V | 1] for its
 //                     queries, and finishes their outputs;
-//   key/state wave s  projects its 16 keys, publishes phi(K) in LDS, holds
-//                     the state slice G[:, 16s..16s+15] (all m features) and
+//   key/state wave s  projects all 64 keys over the feature tiles
+//                     ft = s (mod 4) (its projection operands stay in
+//                     registers), publishes phi(K) in LDS, holds the state
+//                     slice G[:, 16s..16s+15] (all m features) and
 //                     z for the feature blocks kb = s (mod 4) in fp32
 //                     registers, computes the inter-chunk terms phi(Q) G for
 //                     all 64 queries (published in LDS) and updates G and z.
