@@ -49,6 +49,9 @@ __device__ __forceinline__ f4 mma32(f8 a, f8 b, f4 c) {
 
 __device__ __forceinline__ f4 f4splat(float x) { return f4{x, x, x, x}; }
 
+// compile-time integer, to pick a specialised code path from a run-time value
+template <int N> struct IntC { static constexpr int value = N; };
+
 // Pack two D tiles' 4-element columns into one 8-slot operand (kappa order).
 __device__ __forceinline__ bf16x8 pack8(bf16, f4 lo, f4 hi) {
     bf16x8 r;

@@ -1131,12 +1131,27 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
                     xq[ks] = *reinterpret_cast<const bf16x8*>(tq + off_row + 16 * s * RS + 32 * ks);
+                // projection operands from LDS, read one group of feature
+                // tiles ahead of their products
+                constexpr int GF = 2, NG = NFT / GF, GO = GF * KSD;
                 f4 pq[NFT];
+                bf16x8 oa[2][GO];
 #pragma unroll
-                for (int ft = 0; ft < NFT; ++ft) {
-                    pq[ft] = f4splat(cq);
+                for (int i = 0; i < GO; ++i) oa[0][i] = om[i * 64 + lane];
 #pragma unroll
-                    for (int ks = 0; ks < KSD; ++ks) pq[ft] = mma32(om[(ft * KSD + ks) * 64 + lane], xq[ks], pq[ft]);
+                for (int gi = 0; gi < NG; ++gi) {
+                    if (gi + 1 < NG) {
+#pragma unroll
+                        for (int i = 0; i < GO; ++i) oa[(gi + 1) & 1][i] = om[((gi + 1) * GO + i) * 64 + lane];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int f = 0; f < GF; ++f) {
+                        const int ft = gi * GF + f;
+                        pq[ft] = f4splat(cq);
+#pragma unroll
+                        for (int ks = 0; ks < KSD; ++ks) pq[ft] = mma32(oa[gi & 1][f * KSD + ks], xq[ks], pq[ft]);
+                    }
                 }
                 float mx = kNegInf;
 #pragma unroll
@@ -1163,42 +1178,59 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
             prefetch_chunk(c + 2);
 
             // ---- intra-chunk terms for queries 16s..16s+15: key tiles 0..s
-            // (later ones are all masked), keys after the query zeroed
-            f4 st[4];
+            // (later ones are all masked), keys after the query zeroed.  One
+            // code path per s, so the products of the s + 1 key tiles form
+            // independent accumulation chains issued feature block by block.
+            auto intra = [&](auto nkt_c) {
+                constexpr int NKT = decltype(nkt_c)::value;
+                constexpr int NA = NKT <= 2 ? 2 : 1;  // partial sums per key tile
+                f4 sa[NKT][NA];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                st[kt] = f4splat(0.0f);
-                if (kt <= s) {
-                    // all operand reads of the tile first, then the products
-                    const bf16* pr = phk + off_krow + 16 * kt * PKS;
-                    bf16x8 a[NFB];
+                for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                    for (int kb = 0; kb < NFB; ++kb) {
-                        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(pr + 32 * kb);
-                        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(pr + 32 * kb + 16);
-                        a[kb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    for (int a = 0; a < NA; ++a) sa[kt][a] = f4splat(0.0f);
+                auto read_a = [&](int kb, bf16x8* a) {
+#pragma unroll
+                    for (int kt = 0; kt < NKT; ++kt) {
+                        const bf16* pr = phk + off_krow + 16 * kt * PKS + 32 * kb;
+                        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(pr);
+                        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(pr + 16);
+                        a[kt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     }
-                    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+                };
+                bf16x8 a[2][NKT];
+                read_a(0, a[0]);
 #pragma unroll
-                    for (int kb = 0; kb < NFB; ++kb) st[kt] = mma32(a[kb], bq[kb], st[kt]);
-                    if (kt == s) {
+                for (int kb = 0; kb < NFB; ++kb) {
+                    if (kb + 1 < NFB) read_a(kb + 1, a[(kb + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (4 * g + i > r) st[kt][i] = 0.0f;
-                    }
+                    for (int kt = 0; kt < NKT; ++kt) sa[kt][kb % NA] = mma32(a[kb & 1][kt], bq[kb], sa[kt][kb % NA]);
                 }
-            }
+                f4 st[4];
 #pragma unroll
-            for (int ct = 0; ct < 5; ++ct) oi[ct] = f4splat(0.0f);
+                for (int kt = 0; kt < 4; ++kt) st[kt] = f4splat(0.0f);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (2 * j <= s) {
+                for (int kt = 0; kt < NKT; ++kt) st[kt] = NA == 2 ? sa[kt][0] + sa[kt][NA - 1] : sa[kt][0];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g + i > r) st[NKT - 1][i] = 0.0f;
+#pragma unroll
+                for (int ct = 0; ct < 5; ++ct) oi[ct] = f4splat(0.0f);
+#pragma unroll
+                for (int j = 0; j < (NKT + 1) / 2; ++j) {
                     const bf16x8 b = pack8t<bf16>(st[2 * j], st[2 * j + 1]);
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct)
                         oi[ct] = mma32(kappa_col_at<RS>(tv + off_trv + 32 * j * RS + 16 * ct), b, oi[ct]);
                     oi[4] = mma32(ones, b, oi[4]);
                 }
+            };
+            switch (s) {
+                case 0: intra(IntC<1>{}); break;
+                case 1: intra(IntC<2>{}); break;
+                case 2: intra(IntC<3>{}); break;
+                default: intra(IntC<4>{}); break;
             }
             __syncthreads();
         }
@@ -1248,7 +1280,9 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
             stage_chunk(c + 1);
             prefetch_chunk(c + 2);
 
-            // ---- inter-chunk terms phi(Q) G for all 64 queries
+            // ---- inter-chunk terms phi(Q) G for all 64 queries: the four
+            // query tiles are independent accumulation chains, advanced
+            // feature block by feature block
             {
                 bf16x8 ga[NFB];
 #pragma unroll
@@ -1256,23 +1290,33 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
                 bf16x8 za[ZB];
 #pragma unroll
                 for (int zb = 0; zb < ZB; ++zb) za[zb] = pack8t<bf16>(Z[2 * zb], Z[2 * zb + 1]);
+                f4 o[4], dz[4];
 #pragma unroll
                 for (int qt = 0; qt < 4; ++qt) {
-                    // all operand reads of the query tile first, then the products
-                    bf16x8 b[NFB];
+                    o[qt] = f4splat(0.0f);
+                    dz[qt] = f4splat(0.0f);
+                }
 #pragma unroll
-                    for (int kb = 0; kb < NFB; ++kb) b[kb] = phq[(qt * NFB + kb) * 64 + lane];
-                    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-                    f4 o = f4splat(0.0f);
+                for (int kb = 0; kb < NFB; ++kb) {
+                    bf16x8 b[4];
 #pragma unroll
-                    for (int kb = 0; kb < NFB; ++kb) o = mma32(ga[kb], b[kb], o);
-                    *reinterpret_cast<f4*>(oin + (16 * qt + r) * OS + 16 * s + 4 * g) = o;
-                    // z blocks past m are zero (their index is clamped for the read)
-                    f4 dz = f4splat(0.0f);
+                    for (int qt = 0; qt < 4; ++qt) b[qt] = phq[(qt * NFB + kb) * 64 + lane];
 #pragma unroll
-                    for (int zb = 0; zb < ZB; ++zb)
-                        dz = mma32(za[zb], phq[(qt * NFB + min(s + 4 * zb, NFB - 1)) * 64 + lane], dz);
-                    if (g == 0 && s < NFB) dpart[s * 64 + 16 * qt + r] = dz[0];
+                    for (int qt = 0; qt < 4; ++qt) o[qt] = mma32(ga[kb], b[qt], o[qt]);
+                }
+                // z blocks past m are zero (their index is clamped for the read)
+#pragma unroll
+                for (int zb = 0; zb < ZB; ++zb) {
+                    bf16x8 b[4];
+#pragma unroll
+                    for (int qt = 0; qt < 4; ++qt) b[qt] = phq[(qt * NFB + min(s + 4 * zb, NFB - 1)) * 64 + lane];
+#pragma unroll
+                    for (int qt = 0; qt < 4; ++qt) dz[qt] = mma32(za[zb], b[qt], dz[qt]);
+                }
+#pragma unroll
+                for (int qt = 0; qt < 4; ++qt) {
+                    *reinterpret_cast<f4*>(oin + (16 * qt + r) * OS + 16 * s + 4 * g) = o[qt];
+                    if (g == 0 && s < NFB) dpart[s * 64 + 16 * qt + r] = dz[qt][0];
                 }
             }
             // ---- state update G += phi(K)^T V, z += phi(K)^T 1
@@ -1280,8 +1324,16 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
             for (int j = 0; j < 2; ++j) {
                 const bf16* pj = phk + off_trk + 32 * j * PKS;
                 const bf16x8 bv = kappa_col_at<RS>(tv + off_trv + 32 * j * RS + 16 * s);
+                // phi(K) operands read two feature tiles ahead of their products
+                bf16x8 ka[3];
+                ka[0] = kappa_col_at<PKS>(pj);
+                if (NFT > 1) ka[1] = kappa_col_at<PKS>(pj + 16);
 #pragma unroll
-                for (int ft = 0; ft < NFT; ++ft) G[ft] = mma32(kappa_col_at<PKS>(pj + 16 * ft), bv, G[ft]);
+                for (int ft = 0; ft < NFT; ++ft) {
+                    if (ft + 2 < NFT) ka[(ft + 2) % 3] = kappa_col_at<PKS>(pj + 16 * (ft + 2));
+                    __builtin_amdgcn_sched_barrier(0);
+                    G[ft] = mma32(ka[ft % 3], bv, G[ft]);
+                }
 #pragma unroll
                 for (int zt = 0; zt < 2 * ZB; ++zt) {
                     const int ft = min(2 * (s + 4 * (zt / 2)) + (zt % 2), NFT - 1);
