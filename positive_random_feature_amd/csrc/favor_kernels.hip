@@ -1032,9 +1032,12 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
     float* oin = reinterpret_cast<float*>(smem_raw + SM::OFF_OI);
     float* dpart = reinterpret_cast<float*>(smem_raw + SM::OFF_DP);
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
-    const int s = w & 3;            // token tile and value-column tile of this wave
-    const bool qwave = w < 4;       // query wave (else key/state wave)
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    // wave index, wave-uniform for the compiler: branches on it are scalar
+    // and skip their matrix instructions
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int s = w & 3;       // token tile and value-column tile of this wave
+    const bool qwave = w < 4;  // query wave (else key/state wave)
     const int seg = blockIdx.x, bh = blockIdx.y, h = bh % H;
     const int t_begin = seg * seg_len;
     const int t_end = min(L, t_begin + seg_len);
@@ -1042,9 +1045,11 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
     const size_t xbase = (size_t)bh * L * D;
     const bf16* src[3] = {k + xbase, q + xbase, v + xbase};
 
+    // Q, K, V tiles are loaded and staged by the query waves alone (the
+    // key/state waves carry the longer chain between the two barriers);
     // chunk 0 into registers
-    Prefetch<bf16, D, 512, 3, 64> pf;
-    pf.load(src, t_begin, L - 1);
+    Prefetch<bf16, D, 256, 3, 64> pf;
+    if (qwave) pf.load(src, t_begin, L - 1);
 
     // projection operands of this head into LDS
     {
@@ -1091,8 +1096,10 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
     };
     auto prefetch_chunk = [&](int ci) { pf.load(src, t_begin + 64 * min(ci, nch - 1), L - 1); };
 
-    stage_chunk(0);
-    prefetch_chunk(1);
+    if (qwave) {
+        stage_chunk(0);
+        prefetch_chunk(1);
+    }
     __syncthreads();
 
     const bf16x8 ones = splat8<bf16>(1.0f);
@@ -1236,20 +1243,20 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
         }
         finalize(nch - 1);
     } else {
-        // key/state wave: feature tiles ft = s + 4 f of the key projection
-        // (their projection operands stay in registers), the state slice for
-        // value columns 16s.. and z for feature blocks kb = s + 4 zb
+        // key/state wave: feature tiles ft = s + 4 f of the key projection,
+        // the state slice for value columns 16s.. and z for feature blocks
+        // kb = s + 4 zb
         constexpr int KFT = (NFT + 3) / 4;
-        vec8<bf16> omr[KFT][KSD];
-#pragma unroll
-        for (int f = 0; f < KFT; ++f)
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) omr[f][ks] = om[((s + 4 * f) * KSD + ks) * 64 + lane];
         for (int c = 0; c < nch; ++c) {
             const int t0 = t_begin + 64 * c;
             const bf16* tv = tv0 + (size_t)(c & 1) * SM::TILE;
             // ---- keys of the chunk, this wave's feature tiles, the segment's shift
             {
+                vec8<bf16> omr[KFT][KSD];  // projection operands (from LDS, once per chunk)
+#pragma unroll
+                for (int f = 0; f < KFT; ++f)
+#pragma unroll
+                    for (int ks = 0; ks < KSD; ++ks) omr[f][ks] = om[((s + 4 * f) * KSD + ks) * 64 + lane];
                 f4 pk[4][KFT];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
@@ -1277,41 +1284,34 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
             }
             __syncthreads();
 
-            stage_chunk(c + 1);
-            prefetch_chunk(c + 2);
-
             // ---- inter-chunk terms phi(Q) G for all 64 queries: the four
             // query tiles are independent accumulation chains, advanced
-            // feature block by feature block
+            // feature block by feature block; the denominator terms of this
+            // wave's blocks (kb = s mod 4) reuse the same phi(Q) operands
             {
-                bf16x8 ga[NFB];
-#pragma unroll
-                for (int kb = 0; kb < NFB; ++kb) ga[kb] = pack8t<bf16>(G[2 * kb], G[2 * kb + 1]);
-                bf16x8 za[ZB];
-#pragma unroll
-                for (int zb = 0; zb < ZB; ++zb) za[zb] = pack8t<bf16>(Z[2 * zb], Z[2 * zb + 1]);
                 f4 o[4], dz[4];
 #pragma unroll
                 for (int qt = 0; qt < 4; ++qt) {
                     o[qt] = f4splat(0.0f);
                     dz[qt] = f4splat(0.0f);
                 }
+                bf16x8 b[2][4];
+#pragma unroll
+                for (int qt = 0; qt < 4; ++qt) b[0][qt] = phq[qt * NFB * 64 + lane];
 #pragma unroll
                 for (int kb = 0; kb < NFB; ++kb) {
-                    bf16x8 b[4];
+                    if (kb + 1 < NFB) {
 #pragma unroll
-                    for (int qt = 0; qt < 4; ++qt) b[qt] = phq[(qt * NFB + kb) * 64 + lane];
+                        for (int qt = 0; qt < 4; ++qt) b[(kb + 1) & 1][qt] = phq[(qt * NFB + kb + 1) * 64 + lane];
+                    }
+                    const bf16x8 ga = pack8t<bf16>(G[2 * kb], G[2 * kb + 1]);
 #pragma unroll
-                    for (int qt = 0; qt < 4; ++qt) o[qt] = mma32(ga[kb], b[qt], o[qt]);
-                }
-                // z blocks past m are zero (their index is clamped for the read)
+                    for (int qt = 0; qt < 4; ++qt) o[qt] = mma32(ga, b[kb & 1][qt], o[qt]);
+                    if (kb % 4 == s) {
+                        const bf16x8 za = pack8t<bf16>(Z[2 * (kb / 4)], Z[2 * (kb / 4) + 1]);
 #pragma unroll
-                for (int zb = 0; zb < ZB; ++zb) {
-                    bf16x8 b[4];
-#pragma unroll
-                    for (int qt = 0; qt < 4; ++qt) b[qt] = phq[(qt * NFB + min(s + 4 * zb, NFB - 1)) * 64 + lane];
-#pragma unroll
-                    for (int qt = 0; qt < 4; ++qt) dz[qt] = mma32(za[zb], b[qt], dz[qt]);
+                        for (int qt = 0; qt < 4; ++qt) dz[qt] = mma32(za, b[kb & 1][qt], dz[qt]);
+                    }
                 }
 #pragma unroll
                 for (int qt = 0; qt < 4; ++qt) {
@@ -1334,6 +1334,8 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
                     __builtin_amdgcn_sched_barrier(0);
                     G[ft] = mma32(ka[ft % 3], bv, G[ft]);
                 }
+                // z of this wave's blocks kb = s + 4 zb (tiles past m clamped;
+                // their sums are never used)
 #pragma unroll
                 for (int zt = 0; zt < 2 * ZB; ++zt) {
                     const int ft = min(2 * (s + 4 * (zt / 2)) + (zt % 2), NFT - 1);
