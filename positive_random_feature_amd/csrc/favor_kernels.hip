@@ -147,11 +147,19 @@ struct Prefetch {
             v[i] = gload8(src[tn] + (size_t)t * D + 8 * (cc % CPR));
         }
     }
-    // SWZ: the destination tiles use swz_tile (bf16, D = 64)
+    // SWZ: the destination tiles use swz_tile (bf16, D = 64).  Tiles with
+    // every row valid (the common case, a wave-uniform test) take a copy of
+    // the code without the zeroing selects.
     template <bool SWZ = false>
     __device__ __forceinline__ void store(T* const* dst, float* nrm, int norm_mask, int t0, int t_end) const {
+        if (t0 + ROWS <= t_end)
+            store_rows<SWZ, false>(dst, nrm, norm_mask, t0, t_end);
+        else
+            store_rows<SWZ, true>(dst, nrm, norm_mask, t0, t_end);
+    }
+    template <bool SWZ, bool MASK>
+    __device__ __forceinline__ void store_rows(T* const* dst, float* nrm, int norm_mask, int t0, int t_end) const {
         constexpr int RS = LdsTile<T, D>::RS;
-        const bool full = t0 + ROWS <= t_end;  // uniform: no row needs zeroing
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int c = threadIdx.x + i * NTHR;
@@ -160,7 +168,7 @@ struct Prefetch {
                 where(i, tn, cc);
                 const int row = cc / CPR, col = 8 * (cc % CPR);
                 vec8<T> x = v[i];
-                if (!full && t0 + row >= t_end) x = zero8<T>();
+                if (MASK && t0 + row >= t_end) x = zero8<T>();
                 // a select over constant indices (not dst[tn]) keeps the LDS
                 // address space visible to the compiler: no flat stores
                 T* d = dst[0];
@@ -323,26 +331,34 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
         return lm;
     };
 
+    // projections of two consecutive steps, used in turn with the loop
+    // unrolled by a multiple of two (no copies); with one step in flight
+    // (large d, register-bound) the next step's projection is copied instead
+    f4 pj[2][4][NFT];
+    constexpr bool PING = PD > 1;
+    constexpr int U = !PING ? 1 : (PD % 2 == 0 ? PD : 2 * PD);  // steps per unrolled iteration
+
     // step 0: stage, project, and take its maximum as the shift
-    f4 pc[4][NFT];
     stage(pf[0], 0);
     __syncthreads();
     if (active) {
-        const float tm = wave_max_uniform(project(0, pc));
+        const float tm = wave_max_uniform(project(0, pj[0]));
         M = tm;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int ft = 0; ft < NFT; ++ft) pc[tt][ft] -= tm;
+            for (int ft = 0; ft < NFT; ++ft) pj[0][tt][ft] -= tm;
     }
 
-    for (int i0 = 0; i0 < nsteps; i0 += PD) {
+    for (int i0 = 0; i0 < nsteps; i0 += U) {
 #pragma unroll
-        for (int u = 0; u < PD; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int it = i0 + u;
             stage(pf[(u + 1) % PD], it + 1);
             __syncthreads();
             if (active && it < nsteps) {
+                f4(&pc)[4][NFT] = pj[PING ? (u & 1) : 0];
+                f4(&pn)[4][NFT] = pj[PING ? ((u + 1) & 1) : 1];
                 // this step's features (exponentials of values already relative
                 // to M), the next step's projection and this step's update are
                 // independent and interleave; the shift test for the next step
@@ -360,7 +376,6 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
                         }
                         a[ks2][ft] = pack8t<T>(e0, e1);
                     }
-                f4 pn[4][NFT];
                 float lm = kNegInf;
                 const bool more = it + 1 < nsteps;
                 if (more) lm = project(it + 1, pn);
@@ -391,10 +406,12 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
                         for (int ft = 0; ft < NFT; ++ft) pn[tt][ft] -= tm;
                     M += tm;
                 }
+                if constexpr (!PING) {
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
+                    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                    for (int ft = 0; ft < NFT; ++ft) pc[tt][ft] = pn[tt][ft];
+                        for (int ft = 0; ft < NFT; ++ft) pc[tt][ft] = pn[tt][ft];
+                }
             }
         }
     }
@@ -1471,7 +1488,7 @@ static hipError_t launch_all(const LaunchArgs& a) {
     const int per_head = a.omega_per_head ? 1 : 0;
     const int nfg = (a.m + 255) / 256;
     stage_event(a, 0);
-    constexpr int PD_KV = D >= 128 ? 1 : 3;
+    constexpr int PD_KV = D >= 128 ? 1 : 2;
     hipLaunchKernelGGL((kv_partial_kernel<T, D, PD_KV>), dim3(a.nseg, BH, nfg), dim3(512), 0, st, k, v, a.omega, per_head,
                        a.ws_partial, a.ws_pmax, a.H, a.L, a.m, a.seg_len, a.nseg);
     stage_event(a, 1);
