@@ -107,25 +107,26 @@ template <typename V> __device__ __forceinline__ V gload_vec(const V* p) {
     return *(__attribute__((address_space(1))) const V*)(p);
 }
 
-// Workgroup copy of n 16-byte vectors from global memory to LDS, with the
-// loads of a batch issued before any of its stores (one memory latency per
-// batch instead of one per vector).
-template <int NTHR, int BATCH = 8, typename V>
-__device__ __forceinline__ void copy_to_lds(V* dst, const V* src, int n) {
-    for (int e0 = 0; e0 < n; e0 += NTHR * BATCH) {
-        V x[BATCH];
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-            const int e = e0 + j * NTHR + (int)threadIdx.x;
-            if (e < n) x[j] = gload_vec(src + e);
-        }
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-            const int e = e0 + j * NTHR + (int)threadIdx.x;
-            if (e < n) dst[e] = x[j];
-        }
-    }
+// Workgroup copy of n 16-byte vectors from global memory straight into LDS
+// (global_load_lds_dwordx4: no registers, every load of every thread in
+// flight at once).  Each wave instruction fills 1 KB of consecutive LDS from
+// a wave-uniform base (the lane offset is implicit).  The data is in LDS only
+// after lds_dma_wait() and a barrier.
+template <int NTHR, typename V>
+__device__ __forceinline__ void copy_to_lds_async(V* dst, const V* src, int n) {
+    static_assert(sizeof(V) % 16 == 0, "16-byte vectors");
+    constexpr int P = sizeof(V) / 16;  // 16-byte pieces per vector
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const int n16 = n * P;
+    const int lane = threadIdx.x & 63;
+    const char* s8 = reinterpret_cast<const char*>(src);
+    char* d8 = reinterpret_cast<char*>(dst);
+    for (int e = threadIdx.x; e < n16; e += NTHR)
+        __builtin_amdgcn_global_load_lds(s8 + 16 * (size_t)e, (lds_ptr)(d8 + 16 * (size_t)(e - lane)), 16, 0, 0);
 }
+// Completion of this thread's LDS-direct loads (and of everything else it
+// has outstanding).
+__device__ __forceinline__ void lds_dma_wait() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Lane exchanges (ds_bpermute through __shfl_xor).
 // Sum / max over the four lanes r, r+16, r+32, r+48 (the lanes holding one

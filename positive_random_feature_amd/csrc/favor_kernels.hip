@@ -530,15 +530,15 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// bidir_out: workgroup = 8 waves x (16 NTT) queries.  The projection operands
+// bidir_out: workgroup = NW waves x (16 NTT) queries.  The projection operands
 // (packed omega') and the output operands ([KV | z]^T) of the head are staged
 // once in LDS.  Each wave loops over 32-feature chunks: project its NTT query
 // tiles (D[F x T], lanes own token columns), keep a lazily raised per-query
 // shift (lane-local test; the cross-lane max only when some lane needs it),
 // exponentiate into the B operand and accumulate out^T[dims | z][T].
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool OM_LDS, bool KV_LDS>
-__global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q, const vec8<T>* __restrict__ ompack,
+template <typename T, int D, bool OM_LDS, bool KV_LDS, int NW>
+__global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict__ q, const vec8<T>* __restrict__ ompack,
                                                         long long om_head_vecs, const vec8<T>* __restrict__ kvpack,
                                                         const float* __restrict__ mmax, T* __restrict__ out, int H,
                                                         int L, int m) {
@@ -568,8 +568,8 @@ __global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q,
     }
     const vec8<T>* omh = ompack + (size_t)(om_head_vecs ? h : 0) * (size_t)om_head_vecs;
     const vec8<T>* kvh = kvpack + (size_t)bh * NMT * nfb * 64;
-    if (OM_LDS) copy_to_lds<512>(om_stage, omh, nft * KSD * 64);
-    if (KV_LDS) copy_to_lds<512>(kv_stage, kvh, NMT * nfb * 64);
+    if (OM_LDS) copy_to_lds_async<64 * NW>(om_stage, omh, nft * KSD * 64);
+    if (KV_LDS) copy_to_lds_async<64 * NW>(kv_stage, kvh, NMT * nfb * 64);
     const vec8<T>* om_src = OM_LDS ? om_stage : omh;
     const vec8<T>* kv_src = KV_LDS ? kv_stage : kvh;
     float Mstar = kNegInf;
@@ -587,6 +587,7 @@ __global__ __launch_bounds__(512) void bidir_out_kernel(const T* __restrict__ q,
             }
         cq[tt] = -0.5f * kLog2e * col_sum(ss);
     }
+    lds_dma_wait();
     __syncthreads();
     if (tbase >= L) return;
 
@@ -1062,17 +1063,18 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
     const size_t xbase = (size_t)bh * L * D;
     const bf16* src[3] = {k + xbase, q + xbase, v + xbase};
 
+    // projection operands of this head straight into LDS (complete before
+    // the first barrier)
+    {
+        const bf16x8* omh = ompack + (size_t)(om_head_vecs ? h : 0) * (size_t)om_head_vecs;
+        copy_to_lds_async<512>(om, omh, NFT * KSD * 64);
+    }
+
     // Q, K, V tiles are loaded and staged by the query waves alone (the
     // key/state waves carry the longer chain between the two barriers);
     // chunk 0 into registers
     Prefetch<bf16, D, 256, 3, 64> pf;
     if (qwave) pf.load(src, t_begin, L - 1);
-
-    // projection operands of this head into LDS
-    {
-        const bf16x8* omh = ompack + (size_t)(om_head_vecs ? h : 0) * (size_t)om_head_vecs;
-        copy_to_lds<512>(om, omh, NFT * KSD * 64);
-    }
 
     // carry-in (state waves): state slice for columns 16s.. and z for this
     // wave's blocks, rescaled from the per-block shifts to the segment's
@@ -1115,7 +1117,10 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
 
     if (qwave) {
         stage_chunk(0);
+        lds_dma_wait();
         prefetch_chunk(1);
+    } else {
+        lds_dma_wait();
     }
     __syncthreads();
 
@@ -1500,24 +1505,27 @@ static hipError_t launch_all(const LaunchArgs& a) {
     stage_event(a, 2);
     if (a.op == OpKind::Bidir) {
         constexpr int NTT = 2;
-        const int tok_per_wg = 8 * 16 * NTT;
+        // waves per workgroup: sixteen where the registers allow (bf16,
+        // d <= 64), so each staging of the operands serves 512 queries
+        constexpr int NW = (sizeof(T) == 2 && D <= 64) ? 16 : 8;
+        const int tok_per_wg = NW * 16 * NTT;
         const int blocks = (a.L + tok_per_wg - 1) / tok_per_wg;
         const size_t om_b = sizeof(vec8<T>) * 64 * (size_t)(a.m / 16) * KSD;
         const size_t kv_b = sizeof(vec8<T>) * 64 * (size_t)(D / 16 + 1) * (a.m / 32);
         const vec8<T>* kvp = reinterpret_cast<const vec8<T>*>(a.ws_kvpack);
         if (om_b + kv_b <= kMaxLds) {
-            auto kern = bidir_out_kernel<T, D, true, true>;
+            auto kern = bidir_out_kernel<T, D, true, true, NW>;
             (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(om_b + kv_b));
-            hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(512), om_b + kv_b, st, q, ompack, om_head_vecs, kvp,
+            hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), om_b + kv_b, st, q, ompack, om_head_vecs, kvp,
                                a.ws_mmax, out, a.H, a.L, a.m);
         } else if (kv_b <= kMaxLds) {
-            auto kern = bidir_out_kernel<T, D, false, true>;
+            auto kern = bidir_out_kernel<T, D, false, true, NW>;
             (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kv_b);
-            hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(512), kv_b, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,
+            hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), kv_b, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,
                                out, a.H, a.L, a.m);
         } else {
-            auto kern = bidir_out_kernel<T, D, false, false>;
-            hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(512), 0, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,
+            auto kern = bidir_out_kernel<T, D, false, false, NW>;
+            hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), 0, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,
                                out, a.H, a.L, a.m);
         }
         stage_event(a, 3);
