@@ -8,6 +8,9 @@ namespace favor {
 
 // LDS available to one workgroup on gfx950.
 constexpr size_t kMaxLds = 160 * 1024;
+// Most segments per head the launch plan makes (the merge/scan pass keeps
+// their shifts in LDS).
+constexpr int kMaxSeg = 256;
 
 enum class OpKind { Features, Bidir, Causal };
 

@@ -473,9 +473,15 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
     const size_t o = mt < NTV ? seg_v_off<D>(ft, mt, lane) : (size_t)m * D + 16 * ft + 4 * g;
     constexpr int NB = 8;  // segments loaded per batch
 
+    // the block's segment shifts, gathered once into LDS (one load each, all
+    // in flight together, instead of a dependent scalar load per segment)
+    __shared__ float pms[kMaxSeg];
+    for (int s = threadIdx.x; s < nseg; s += blockDim.x) pms[s] = pm[(size_t)s * nfb + fb];
+    __syncthreads();
+
     if (mode == 0) {
         float Ms = kNegInf;
-        for (int s = 0; s < nseg; ++s) Ms = __builtin_fmaxf(Ms, pm[(size_t)s * nfb + fb]);
+        for (int s = 0; s < nseg; ++s) Ms = __builtin_fmaxf(Ms, pms[s]);
         f4 acc = f4splat(0.0f);
         for (int s0 = 0; s0 < nseg; s0 += NB) {
             f4 x[NB];
@@ -484,7 +490,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
                 x[j] = *reinterpret_cast<const f4*>(pb + (size_t)min(s0 + j, nseg - 1) * seg_stride + o);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const float ms = s0 + j < nseg ? pm[(size_t)(s0 + j) * nfb + fb] : kNegInf;
+                const float ms = s0 + j < nseg ? pms[s0 + j] : kNegInf;
                 acc += (ms == kNegInf ? 0.0f : exp2f_fast(ms - Ms)) * x[j];
             }
         }
@@ -509,7 +515,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
             for (int j = 0; j < NB; ++j) {
                 const int s = s0 + j;
                 if (s < nseg) {
-                    const float ms = pm[(size_t)s * nfb + fb];
+                    const float ms = pms[s];
                     if (ms > Mrun) {
                         acc *= (Mrun == kNegInf ? 0.0f : exp2f_fast(Mrun - ms));
                         Mrun = ms;
@@ -519,10 +525,11 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
                 }
             }
         }
-        if (threadIdx.x == 0 && half == 0) {
-            float Mr = kNegInf;
-            for (int s = 0; s < nseg; ++s) {
-                Mr = __builtin_fmaxf(Mr, pm[(size_t)s * nfb + fb]);
+        if (half == 0) {
+            // running maxima: thread s takes the maximum over segments <= s
+            for (int s = threadIdx.x; s < nseg; s += blockDim.x) {
+                float Mr = kNegInf;
+                for (int u = 0; u <= s; ++u) Mr = __builtin_fmaxf(Mr, pms[u]);
                 cmax[((size_t)bh * nseg + s) * nfb + fb] = Mr;
             }
         }
