@@ -1168,10 +1168,17 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
                 for (int ks = 0; ks < KSD; ++ks)
                     xq[ks] = *reinterpret_cast<const bf16x8*>(tq + off_row + 16 * s * RS + 32 * ks);
                 // projection operands from LDS, read one group of feature
-                // tiles ahead of their products
+                // tiles ahead of their products.  The per-query shift is the
+                // maximum over the first NF0 feature tiles; it is folded into
+                // the initialisation of the remaining tiles (no subtraction
+                // there), which are only checked against it: a query whose
+                // later features exceed it by more than kTau raises its shift
+                // (rare), so every value stays <= 2^kTau.
                 constexpr int GF = 2, NG = NFT / GF, GO = GF * KSD;
+                constexpr int NF0 = NFT < 4 ? NFT : 4;  // tiles that set the shift
                 f4 pq[NFT];
                 bf16x8 oa[2][GO];
+                float mx = kNegInf;
 #pragma unroll
                 for (int i = 0; i < GO; ++i) oa[0][i] = om[i * 64 + lane];
 #pragma unroll
@@ -1180,28 +1187,52 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
 #pragma unroll
                         for (int i = 0; i < GO; ++i) oa[(gi + 1) & 1][i] = om[((gi + 1) * GO + i) * 64 + lane];
                     }
+                    if (gi * GF == NF0) {  // the first NF0 tiles are done: their maximum
+#pragma unroll
+                        for (int ft = 0; ft < NF0; ++ft)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[ft][i]);
+                        mx = col_max(mx);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int f = 0; f < GF; ++f) {
                         const int ft = gi * GF + f;
-                        pq[ft] = f4splat(cq);
+                        pq[ft] = f4splat(ft < NF0 ? cq : cq - mx);
 #pragma unroll
                         for (int ks = 0; ks < KSD; ++ks) pq[ft] = mma32(oa[gi & 1][f * KSD + ks], xq[ks], pq[ft]);
                     }
                 }
-                float mx = kNegInf;
+                if constexpr (NF0 == NFT) {
 #pragma unroll
-                for (int ft = 0; ft < NFT; ++ft)
+                    for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[ft][i]);
-                mx = col_max(mx);
+                        for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[ft][i]);
+                    mx = col_max(mx);
+                }
+#pragma unroll
+                for (int ft = 0; ft < NF0; ++ft) pq[ft] -= mx;
+                if constexpr (NF0 < NFT) {
+                    float lm = kNegInf;
+#pragma unroll
+                    for (int ft = NF0; ft < NFT; ++ft)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) lm = __builtin_fmaxf(lm, pq[ft][i]);
+                    if (wave_any(lm > kTau)) {
+                        // raise the shift of the queries that need it
+                        const float cm = col_max(lm);
+                        const float up = cm > kTau ? cm : 0.0f;
+#pragma unroll
+                        for (int ft = 0; ft < NFT; ++ft) pq[ft] -= up;
+                    }
+                }
 #pragma unroll
                 for (int kb = 0; kb < NFB; ++kb) {
                     f4 e0, e1;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        e0[i] = exp2f_fast(pq[2 * kb][i] - mx);
-                        e1[i] = exp2f_fast(pq[2 * kb + 1][i] - mx);
+                        e0[i] = exp2f_fast(pq[2 * kb][i]);
+                        e1[i] = exp2f_fast(pq[2 * kb + 1][i]);
                     }
                     bq[kb] = pack8t<bf16>(e0, e1);
                     phq[(s * NFB + kb) * 64 + lane] = bq[kb];

@@ -153,6 +153,35 @@ def test_causal_ragged_segments(d, m, B, H, L):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("name,op", [("causal_bf16_8k", "causal"), ("bidir_bf16_4k", "bidir")])
+def test_late_features_raise_query_shift(name, op):
+    """Queries aligned with a feature far from the first feature tiles: the
+    feature that dominates lies beyond the tiles (causal) or chunk (bidir)
+    that set a query's stabiliser, so the kernels must raise it (Simple
+    Derivation: any per-query factor cancels).  Every element."""
+    from positive_random_feature_amd.workloads import bf16_bits_to_f32, f32_to_bf16_bits
+    w = WORKLOADS[name]
+    B, H, L = 1, 2, 700
+    inp = make_inputs(w, B=B, H=H, L=L)
+    om = _omega(w, H)
+    q = inp.q.copy()
+    for h in range(H):
+        o = om[h] if w.omega_per_head else om
+        f = w.m - 40 - 7 * h  # a feature in the last tiles
+        u = o[f] / np.linalg.norm(o[f])
+        q[0, h, ::7] = (3.0 * u).astype(np.float32)
+    inp.q_bits = f32_to_bf16_bits(q.astype(np.float32))
+    inp.q = bf16_bits_to_f32(inp.q_bits)
+    qd, kd, vd = _to_dev(inp, w.dtype)
+    fn = favor.bidir if op == "bidir" else favor.causal
+    got = fn(qd, kd, vd, torch.from_numpy(om).to(_dev())).float().cpu().numpy().astype(np.float64)
+    want = (native.bidir if op == "bidir" else native.causal)(inp.q, inp.k, inp.v, om)
+    err = _rel(got, want)
+    _log(f"{name} {op} late-feature queries", err, TOL["bf16"])
+    assert np.isfinite(got).all()
+    assert err <= TOL["bf16"]
+
+
 def test_causal_prefix_invariance():
     """Causal outputs of a prefix do not depend on later tokens, whatever the
     segmentation chosen for the two lengths."""
