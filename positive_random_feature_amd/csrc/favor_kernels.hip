@@ -1344,10 +1344,13 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
             }
             __syncthreads();
 
-            // ---- inter-chunk terms phi(Q) G for all 64 queries: the four
-            // query tiles are independent accumulation chains, advanced
-            // feature block by feature block; the denominator terms of this
-            // wave's blocks (kb = s mod 4) reuse the same phi(Q) operands
+            // ---- inter-chunk terms phi(Q) G for all 64 queries and the state
+            // update G += phi(K)^T V, z += phi(K)^T 1, interleaved feature
+            // block by feature block: block kb's inter-chunk products use G
+            // of the previous chunks (packed before its update), then its two
+            // feature tiles are updated.  The four query tiles are
+            // independent accumulation chains; the denominator terms and z of
+            // this wave's blocks (kb = s mod 4) reuse the same operands.
             {
                 f4 o[4], dz[4];
 #pragma unroll
@@ -1355,51 +1358,51 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
                     o[qt] = f4splat(0.0f);
                     dz[qt] = f4splat(0.0f);
                 }
-                bf16x8 b[2][4];
+                bf16x8 bv[2];  // V operand of this wave's columns, both token halves
 #pragma unroll
-                for (int qt = 0; qt < 4; ++qt) b[0][qt] = phq[qt * NFB * 64 + lane];
+                for (int jj = 0; jj < 2; ++jj) bv[jj] = kappa_col_at<RS>(tv + off_trv + 32 * jj * RS + 16 * s);
+                // operands of block kb: phi(Q) for the four query tiles, phi(K)^T
+                // for its two feature tiles and both token halves (read one
+                // block ahead of their products)
+                bf16x8 b[2][4], ka[2][4];
+                auto read_block = [&](int kb, bf16x8* bb, bf16x8* kk) {
+#pragma unroll
+                    for (int qt = 0; qt < 4; ++qt) bb[qt] = phq[(qt * NFB + kb) * 64 + lane];
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj)
+                            kk[2 * hf + jj] = kappa_col_at<PKS>(phk + off_trk + 32 * jj * PKS + 16 * (2 * kb + hf));
+                };
+                read_block(0, b[0], ka[0]);
 #pragma unroll
                 for (int kb = 0; kb < NFB; ++kb) {
-                    if (kb + 1 < NFB) {
-#pragma unroll
-                        for (int qt = 0; qt < 4; ++qt) b[(kb + 1) & 1][qt] = phq[(qt * NFB + kb + 1) * 64 + lane];
-                    }
+                    if (kb + 1 < NFB) read_block(kb + 1, b[(kb + 1) & 1], ka[(kb + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const bf16x8* bb = b[kb & 1];
+                    const bf16x8* kk = ka[kb & 1];
                     const bf16x8 ga = pack8t<bf16>(G[2 * kb], G[2 * kb + 1]);
 #pragma unroll
-                    for (int qt = 0; qt < 4; ++qt) o[qt] = mma32(ga, b[kb & 1][qt], o[qt]);
-                    if (kb % 4 == s) {
-                        const bf16x8 za = pack8t<bf16>(Z[2 * (kb / 4)], Z[2 * (kb / 4) + 1]);
+                    for (int qt = 0; qt < 4; ++qt) o[qt] = mma32(ga, bb[qt], o[qt]);
 #pragma unroll
-                        for (int qt = 0; qt < 4; ++qt) dz[qt] = mma32(za, b[kb & 1][qt], dz[qt]);
+                    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) G[2 * kb + hf] = mma32(kk[2 * hf + jj], bv[jj], G[2 * kb + hf]);
+                    if (kb % 4 == s) {
+                        const int zt = 2 * (kb / 4);
+                        const bf16x8 za = pack8t<bf16>(Z[zt], Z[zt + 1]);
+#pragma unroll
+                        for (int qt = 0; qt < 4; ++qt) dz[qt] = mma32(za, bb[qt], dz[qt]);
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                            for (int jj = 0; jj < 2; ++jj) Z[zt + hf] = mma32(kk[2 * hf + jj], ones, Z[zt + hf]);
                     }
                 }
 #pragma unroll
                 for (int qt = 0; qt < 4; ++qt) {
                     *reinterpret_cast<f4*>(oin + (16 * qt + r) * OS + 16 * s + 4 * g) = o[qt];
                     if (g == 0 && s < NFB) dpart[s * 64 + 16 * qt + r] = dz[qt][0];
-                }
-            }
-            // ---- state update G += phi(K)^T V, z += phi(K)^T 1
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bf16* pj = phk + off_trk + 32 * j * PKS;
-                const bf16x8 bv = kappa_col_at<RS>(tv + off_trv + 32 * j * RS + 16 * s);
-                // phi(K) operands read two feature tiles ahead of their products
-                bf16x8 ka[3];
-                ka[0] = kappa_col_at<PKS>(pj);
-                if (NFT > 1) ka[1] = kappa_col_at<PKS>(pj + 16);
-#pragma unroll
-                for (int ft = 0; ft < NFT; ++ft) {
-                    if (ft + 2 < NFT) ka[(ft + 2) % 3] = kappa_col_at<PKS>(pj + 16 * (ft + 2));
-                    __builtin_amdgcn_sched_barrier(0);
-                    G[ft] = mma32(ka[ft % 3], bv, G[ft]);
-                }
-                // z of this wave's blocks kb = s + 4 zb (tiles past m clamped;
-                // their sums are never used)
-#pragma unroll
-                for (int zt = 0; zt < 2 * ZB; ++zt) {
-                    const int ft = min(2 * (s + 4 * (zt / 2)) + (zt % 2), NFT - 1);
-                    Z[zt] = mma32(kappa_col_at<PKS>(pj + 16 * ft), ones, Z[zt]);
                 }
             }
             __syncthreads();
