@@ -7,6 +7,16 @@ resident in device memory.  The metric is tokens (B*H*L) per second over the
 whole step.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Besides the step, every workload (the small fp32 case, the two long
+bidirectional ones, the two long causal ones) is timed on its own and
+reported under "configs" with its algorithmic work and roofline fraction.
+
+``python bench.py --summarise-counters FETCH_DIR WRITE_DIR`` turns two
+rocprofv3 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of this script
+(with ``--calib-copy --no-configs``) into profiles/traffic.json;
+``python bench.py --summarise-trace TRACE_DIR`` prints per-stage launch
+times from a ``--kernel-trace`` run.
 """
 
 from __future__ import annotations
@@ -31,6 +41,8 @@ from positive_random_feature_amd import _lib  # noqa: E402
 from positive_random_feature_amd.workloads import WORKLOADS, make_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+# dense matrix-core peaks (TFLOP/s) by operand dtype
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # kernels of the three stages of each op at the bench shapes (d=64, m=256)
 STAGES = {"bidir": ["kv_partial", "merge_scan", "bidir_out"],
           "causal": ["kv_partial", "merge_scan", "causal_tile"]}
@@ -76,7 +88,10 @@ class Op:
         w = self.w
         inp = make_inputs(w)
         self.inp = inp
-        self.q, self.k, self.v = (to_dev_bf16(b, dev) for b in (inp.q_bits, inp.k_bits, inp.v_bits))
+        if w.dtype == "bf16":
+            self.q, self.k, self.v = (to_dev_bf16(b, dev) for b in (inp.q_bits, inp.k_bits, inp.v_bits))
+        else:
+            self.q, self.k, self.v = (torch.from_numpy(a).to(dev) for a in (inp.q, inp.k, inp.v))
         om = favor.orf_omega(w.seed, w.H if w.omega_per_head else 1, w.m, w.d)
         self.omega_host = om.numpy() if w.omega_per_head else om[0].numpy()
         self.omega = (om if w.omega_per_head else om[0]).contiguous().to(dev)
@@ -140,25 +155,168 @@ def traffic_for(stage: str, src_hash: str):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(ops):
-    """The plain-C fp64 oracle on the host cores, over one full step's inputs."""
+def cpu_baseline(ops, min_seconds: float = 10.0, max_rounds: int = 50):
+    """The plain-C fp64 oracle on the host cores, over whole steps' inputs,
+    repeated until at least ``min_seconds`` of CPU work have been timed."""
     from oracle import native
     native.build(force=False)
     t_total = 0.0
     tokens = 0
-    for op in ops:
-        inp = op.inp
-        fn = native.bidir if op.w.op == "bidir" else native.causal
-        runs = []
-        for _ in range(3):
+    rounds = 0
+    while rounds < max_rounds and (rounds == 0 or t_total < min_seconds):
+        for op in ops:
+            inp = op.inp
+            fn = native.bidir if op.w.op == "bidir" else native.causal
             t0 = time.perf_counter()
             fn(inp.q, inp.k, inp.v, op.omega_host)
-            runs.append(time.perf_counter() - t0)
-        t_total += sorted(runs)[1]
-        tokens += op.w.tokens
+            t_total += time.perf_counter() - t0
+            tokens += op.w.tokens
+        rounds += 1
     return {"value": tokens / t_total, "unit": "tokens/s", "cores": native.num_threads(), "kind": "oracle",
-            "sample": "one full step (bidir 4x8x4096 + causal 2x8x8192, d=64, m=256), median of 3 runs per op, "
+            "sample": f"{rounds} full steps (bidir 4x8x4096 + causal 2x8x8192, d=64, m=256) back to back, "
                       "fp64 plain-C oracle, OpenMP over heads", "seconds": t_total}
+
+
+def alg_work(w):
+    """Algorithmic FLOPs and HBM bytes of one call: per token 8md + 4m FLOPs
+    (projections of q and k, phi(K)^T [V | 1], phi(Q) [KV | z]) and 4d
+    elements moved (q, k, v read, out written), plus the projection read once
+    per head (fp32)."""
+    elem = 2 if w.dtype == "bf16" else 4
+    flops = w.tokens * (8 * w.m * w.d + 4 * w.m)
+    n_omega = w.H if w.omega_per_head else 1
+    bytes_ = w.tokens * 4 * w.d * elem + n_omega * w.m * w.d * 4
+    return flops, bytes_
+
+
+def time_configs(hip, dev, stream, reps_target_ms: float = 20.0):
+    """Each workload on its own: per-call time (events around back-to-back
+    calls on one stream) and its fraction of the binding roofline."""
+    res = {}
+    for name, w in WORKLOADS.items():
+        op = Op(name, dev)
+        for _ in range(3):
+            op.run(stream)
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        op.run(stream)
+        hip.record(e1, stream)
+        one = max(hip.elapsed_ms(e0, e1), 1e-3)
+        n = int(min(2000, max(5, reps_target_ms / one)))
+        hip.record(e0, stream)
+        for _ in range(n):
+            op.run(stream)
+        hip.record(e1, stream)
+        ms = hip.elapsed_ms(e0, e1) / n
+        flops, bytes_ = alg_work(w)
+        t_mfma = flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
+        t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
+        bound = "mfma" if t_mfma > t_hbm else "hbm"
+        t_roof = max(t_mfma, t_hbm)
+        res[name] = {"op": w.op, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "m": w.m, "dtype": w.dtype,
+                     "calls": n, "us_per_call": ms * 1e3, "tokens_per_s": w.tokens / (ms * 1e-3),
+                     "alg_gflop": flops / 1e9, "alg_mb": bytes_ / 1e6, "bound": bound,
+                     "roof_us": t_roof * 1e6, "frac": t_roof / (ms * 1e-3),
+                     "achieved": (bytes_ / (ms * 1e-3) / 1e9) if bound == "hbm" else (flops / (ms * 1e-3) / 1e12),
+                     "achieved_unit": "GB/s" if bound == "hbm" else "TFLOP/s"}
+        del op
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# Profiler summaries (rocprofv3 CSV output of runs of this script)
+# ---------------------------------------------------------------------------
+def _read_csvs(root, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(root, "**", "*" + suffix), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {root}")
+    return rows
+
+
+def _stage_labels(names):
+    """Label the favor kernel launches of bench runs by launch order: each
+    step (and each stage-timed step) runs the bidirectional op, then the
+    causal one, so kv_partial and merge_scan alternate between the two."""
+    seen = {"kv_partial": 0, "merge_scan": 0}
+    labels = []
+    for n in names:
+        k = next((k for k in ("kv_partial", "merge_scan", "bidir_out", "causal_tile") if k + "_kernel" in n), None)
+        if k is None:
+            labels.append(None)
+        elif k in seen:
+            labels.append(("bidir_bf16_4k" if seen[k] % 2 == 0 else "causal_bf16_8k") + ":" + k)
+            seen[k] += 1
+        else:
+            labels.append(("bidir_bf16_4k" if k == "bidir_out" else "causal_bf16_8k") + ":" + k)
+    return labels
+
+
+def summarise_counters(fetch_dir, write_dir):
+    def per_dispatch(root, counter):
+        rows = [r for r in _read_csvs(root, "counter_collection.csv") if r.get("Counter_Name") == counter]
+        by = {}
+        for r in rows:
+            key = int(r["Dispatch_Id"])
+            by.setdefault(key, [r["Kernel_Name"], 0.0])
+            by[key][1] += float(r["Counter_Value"])
+        return [by[k] for k in sorted(by)]
+
+    out = {"source_hash": kernel_source_hash(), "calibration": {}, "stages": {}}
+    copy_kib = (512 << 20) / 1024.0
+    lines = []
+    vals = {}
+    for counter, root in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        disp = per_dispatch(root, counter)
+        other = [v for n, v in disp if "favor" not in n]
+        if not other:
+            raise SystemExit(f"{counter}: no calibration copy dispatch found (run with --calib-copy)")
+        scale = copy_kib / max(other)
+        out["calibration"]["fetch" if counter == "FETCH_SIZE" else "write"] = scale
+        labels = _stage_labels([n for n, _ in disp])
+        acc = {}
+        for (n, v), lab in zip(disp, labels):
+            if lab:
+                acc.setdefault(lab, []).append(v)
+        vals[counter] = {lab: (sum(v) / len(v), scale) for lab, v in acc.items()}
+    for lab in vals["FETCH_SIZE"]:
+        fk, fs = vals["FETCH_SIZE"][lab]
+        wk, wsc = vals["WRITE_SIZE"].get(lab, (0.0, 1.0))
+        b = (fk * fs + wk * wsc) * 1024.0
+        out["stages"][lab] = {"fetch_kib": fk, "write_kib": wk, "bytes_per_launch": b}
+        lines.append(f"| {lab} | {fk:.1f} | {wk:.1f} | {b / 1e6:.2f} |")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"wrote {path}; calibration fetch x{out['calibration']['fetch']:.4f}, "
+          f"write x{out['calibration']['write']:.4f}; source hash {out['source_hash']}")
+    print("| stage (workload:kernel) | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | scaled MB/dispatch |")
+    print("|---|---|---|---|")
+    print("\n".join(lines))
+
+
+def summarise_trace(trace_dir):
+    rows = _read_csvs(trace_dir, "kernel_trace.csv")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = [r["Kernel_Name"] for r in rows]
+    labels = _stage_labels(names)
+    acc = {}
+    for r, lab in zip(rows, labels):
+        if lab:
+            acc.setdefault(lab, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"kernel source hash {kernel_source_hash()}")
+    print("| stage (workload:kernel) | launches | avg us | median us | min us |")
+    print("|---|---|---|---|---|")
+    for lab, v in acc.items():
+        v = sorted(v)
+        print(f"| {lab} | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} | {v[0]:.2f} |")
 
 
 def main():
@@ -169,7 +327,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB device copy first (calibrates HBM counters in profiler runs)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload timings")
+    ap.add_argument("--summarise-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarise-trace", metavar="TRACE_DIR")
     args = ap.parse_args()
+    if args.summarise_counters:
+        summarise_counters(*args.summarise_counters)
+        return
+    if args.summarise_trace:
+        summarise_trace(args.summarise_trace)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this build.",
               file=sys.stderr)
@@ -266,6 +433,8 @@ def main():
         "wall_s_timed_region": wall,
         "kernel_source_hash": src_hash,
     }
+    if not args.no_configs:
+        result["configs"] = time_configs(hip, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(ops)
     print(json.dumps(result), flush=True)
