@@ -1411,6 +1411,305 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// causal_wide: chunked causal scan for bf16, d = 128, m in {256, 512}.  One
+// workgroup of eight waves per (segment, head, half of the value columns);
+// chunks of 32 tokens.  The fp32 state of a head (m x 129) is too large for
+// one wave's registers, and the projection operands (m x 128 bf16) too large
+// for LDS next to the feature buffers, so both are split over the waves:
+//   wave w projects the chunk's queries and keys over its own m/8 features
+//     (operands resident in registers); the per-query shift is the maximum
+//     over all m features, reduced across the waves through LDS (queries
+//     need no |q|^2 term: it is a per-query factor); keys use the segment's
+//     fixed shift;
+//   wave w = 4 fh + ct holds the state slice G[features of half fh][value
+//     columns 16 nt ..] (nt = 4 half + ct) and z for its projection features;
+//   the intra-chunk scores S^T[key][query] are summed over the waves'
+//     feature slices through LDS;
+//   wave (fh, ct) finishes query tile fh of its columns: its inter-chunk
+//     terms over half fh plus its partner's over the other half, S [V | 1],
+//     the denominator (z terms of all waves plus the row sums of S).
+// Both column halves recompute the projections (the price of keeping the
+// state in registers).  Three barriers per chunk: maxima and key features
+// ready; phi(Q), phi(K), score and denominator partials published; next
+// tiles staged, scores reduced and inter-chunk partials exchanged.
+// ---------------------------------------------------------------------------
+template <int M>
+struct WideSmem {
+    static constexpr int D = 128, NFB = M / 32;
+    static constexpr int RS = LdsTile<bf16, D>::RS;  // Q/K/V tile row stride
+    static constexpr int PKS = M + 16;               // phi(K) row stride (bf16)
+    static constexpr size_t TILE = (size_t)32 * RS;  // elements of a 32-row tile
+    static constexpr size_t OFF_TK = 0;
+    static constexpr size_t OFF_TQ = OFF_TK + sizeof(bf16) * TILE;
+    static constexpr size_t OFF_TV = OFF_TQ + sizeof(bf16) * TILE;  // two buffers
+    static constexpr size_t OFF_NRM = OFF_TV + sizeof(bf16) * 2 * TILE;
+    static constexpr size_t OFF_QMAX = OFF_NRM + sizeof(float) * 3 * 32;
+    static constexpr size_t OFF_PQ = OFF_QMAX + sizeof(float) * 8 * 32;
+    static constexpr size_t OFF_PK = OFF_PQ + sizeof(bf16x8) * (size_t)2 * NFB * 64;
+    static constexpr size_t OFF_SP = OFF_PK + sizeof(bf16) * (size_t)32 * PKS;
+    static constexpr size_t OFF_ST = OFF_SP + sizeof(f4) * (size_t)8 * 3 * 64;
+    static constexpr size_t OFF_DP = OFF_ST + sizeof(f4) * (size_t)3 * 64;
+    static constexpr size_t OFF_XO = OFF_DP + sizeof(float) * 8 * 32;
+    static constexpr size_t BYTES = OFF_XO + sizeof(f4) * (size_t)4 * 2 * 64;
+};
+
+template <int M>
+__global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                          const bf16* __restrict__ v, const bf16x8* __restrict__ ompack,
+                                                          long long om_head_vecs, const float* __restrict__ carry,
+                                                          const float* __restrict__ cmax, bf16* __restrict__ out, int H,
+                                                          int L, int seg_len, int nseg) {
+    using SM = WideSmem<M>;
+    constexpr int D = SM::D, KSD = D / 32, NFB = SM::NFB, RS = SM::RS, PKS = SM::PKS;
+    constexpr int D1 = D + 1;
+    constexpr int PFT = M / 128;  // projection feature tiles per wave (features 16 PFT w ..)
+    constexpr int PFB = PFT / 2;  // projection feature blocks per wave
+    constexpr int GFT = M / 32;   // state feature tiles per wave (one half of the features)
+    constexpr int GFB = GFT / 2;
+    static_assert(PFB >= 1, "m >= 256");
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    bf16* tk = reinterpret_cast<bf16*>(smem_raw + SM::OFF_TK);
+    bf16* tq = reinterpret_cast<bf16*>(smem_raw + SM::OFF_TQ);
+    bf16* tv0 = reinterpret_cast<bf16*>(smem_raw + SM::OFF_TV);
+    float* nrm = reinterpret_cast<float*>(smem_raw + SM::OFF_NRM);  // K rows 0..31
+    float* qmax = reinterpret_cast<float*>(smem_raw + SM::OFF_QMAX);
+    bf16x8* phq = reinterpret_cast<bf16x8*>(smem_raw + SM::OFF_PQ);
+    bf16* phk = reinterpret_cast<bf16*>(smem_raw + SM::OFF_PK);
+    f4* spart = reinterpret_cast<f4*>(smem_raw + SM::OFF_SP);
+    f4* stot = reinterpret_cast<f4*>(smem_raw + SM::OFF_ST);
+    float* dpart = reinterpret_cast<float*>(smem_raw + SM::OFF_DP);
+    f4* xo = reinterpret_cast<f4*>(smem_raw + SM::OFF_XO);
+
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ct = w & 3, fh = w >> 2;
+    const int seg = blockIdx.x, bh = blockIdx.y, h = bh % H;
+    const int nt = 4 * (int)blockIdx.z + ct;  // value-column tile of this wave
+    const int t_begin = seg * seg_len;
+    const int t_end = min(L, t_begin + seg_len);
+    const int nch = (t_end - t_begin + 31) / 32;
+    if (nch <= 0) return;  // workgroup-uniform
+    const size_t xbase = (size_t)bh * L * D;
+    const bf16* src[3] = {k + xbase, q + xbase, v + xbase};
+
+    // chunk 0 into registers first (latency overlaps the loads below)
+    Prefetch<bf16, D, 512, 3, 32> pf;
+    pf.load(src, t_begin, L - 1);
+
+    bf16x8 om[PFT][KSD];
+    {
+        const bf16x8* omh = ompack + (size_t)(om_head_vecs ? h : 0) * (size_t)om_head_vecs;
+#pragma unroll
+        for (int f = 0; f < PFT; ++f)
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) om[f][ks] = omh[((PFT * w + f) * KSD + ks) * 64 + lane];
+    }
+
+    // carry-in rescaled from the per-block shifts to the segment's key shift
+    const float* cm = cmax + ((size_t)bh * nseg + seg) * NFB;
+    float Mseg = kNegInf;
+#pragma unroll
+    for (int b = 0; b < NFB; ++b) Mseg = __builtin_fmaxf(Mseg, cm[b]);
+    f4 G[GFT];
+    f4 Z[PFT];
+    {
+        const float* cb = carry + ((size_t)bh * nseg + seg) * (size_t)M * D1;
+#pragma unroll
+        for (int i = 0; i < GFT; ++i) {
+            const int ft = GFT * fh + i;
+            const float mb = cm[ft / 2];
+            const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
+            G[i] = sc * *reinterpret_cast<const f4*>(cb + seg_v_off<D>(ft, nt, lane));
+        }
+#pragma unroll
+        for (int f = 0; f < PFT; ++f) {
+            const int ft = PFT * w + f;
+            const float mb = cm[ft / 2];
+            const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
+            Z[f] = sc * *reinterpret_cast<const f4*>(cb + (size_t)M * D + 16 * ft + 4 * g);
+        }
+    }
+
+    auto stage_chunk = [&](int ci) {
+        const int cc = min(ci, nch - 1);
+        bf16* dst[3] = {tk, tq, tv0 + (size_t)(ci & 1) * SM::TILE};
+        pf.store(dst, nrm, 1, t_begin + 32 * cc, ci < nch ? t_end : -1);
+        pf.load(src, t_begin + 32 * min(ci + 1, nch - 1), L - 1);
+    };
+    stage_chunk(0);
+    __syncthreads();
+
+    const bf16x8 ones = splat8<bf16>(1.0f);
+    for (int c = 0; c < nch; ++c) {
+        const int t0 = t_begin + 32 * c;
+        const bf16* tv = tv0 + (size_t)(c & 1) * SM::TILE;
+
+        // ---- projections over this wave's features
+        f4 pq[2][PFT];
+        bf16x8 ak[2][PFB];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            bf16x8 x[KSD];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks)
+                x[ks] = *reinterpret_cast<const bf16x8*>(tq + (16 * tt + r) * RS + 32 * ks + 8 * g);
+#pragma unroll
+            for (int f = 0; f < PFT; ++f) {
+                pq[tt][f] = f4splat(0.0f);
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) pq[tt][f] = mma32(om[f][ks], x[ks], pq[tt][f]);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int f = 0; f < PFT; ++f)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[tt][f][i]);
+            mx = col_max(mx);
+            if (g == 0) qmax[w * 32 + 16 * tt + r] = mx;
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            bf16x8 x[KSD];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks)
+                x[ks] = *reinterpret_cast<const bf16x8*>(tk + (16 * tt + r) * RS + 32 * ks + 8 * g);
+            const float ck = (t0 + 16 * tt + r < t_end) ? nrm[16 * tt + r] - Mseg : kNegInf;
+            f4 pk[PFT];
+#pragma unroll
+            for (int f = 0; f < PFT; ++f) {
+                pk[f] = f4splat(ck);
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) pk[f] = mma32(om[f][ks], x[ks], pk[f]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk[f][i] = exp2f_fast(pk[f][i]);
+            }
+#pragma unroll
+            for (int b = 0; b < PFB; ++b) ak[tt][b] = pack8t<bf16>(pk[2 * b], pk[2 * b + 1]);
+        }
+        __syncthreads();
+
+        // ---- phi(Q) with the per-query shift, phi(K) rows, score and
+        // denominator partials over this wave's features
+        bf16x8 bq[2][PFB];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            float mq = qmax[16 * tt + r];
+#pragma unroll
+            for (int ww = 1; ww < 8; ++ww) mq = __builtin_fmaxf(mq, qmax[ww * 32 + 16 * tt + r]);
+#pragma unroll
+            for (int b = 0; b < PFB; ++b) {
+                f4 e0, e1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    e0[i] = exp2f_fast(pq[tt][2 * b][i] - mq);
+                    e1[i] = exp2f_fast(pq[tt][2 * b + 1][i] - mq);
+                }
+                bq[tt][b] = pack8t<bf16>(e0, e1);
+                phq[(tt * NFB + PFB * w + b) * 64 + lane] = bq[tt][b];
+                const bf16x8 a = ak[tt][b];
+                bf16* row = phk + (16 * tt + r) * PKS + 16 * (PFT * w + 2 * b) + 4 * g;
+                *reinterpret_cast<bf16x4*>(row) = bf16x4{a[0], a[1], a[2], a[3]};
+                *reinterpret_cast<bf16x4*>(row + 16) = bf16x4{a[4], a[5], a[6], a[7]};
+            }
+        }
+        {
+            f4 sp[3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) sp[i] = f4splat(0.0f);
+#pragma unroll
+            for (int b = 0; b < PFB; ++b) {
+                sp[0] = mma32(ak[0][b], bq[0][b], sp[0]);  // keys 0..15, queries 0..15
+                sp[1] = mma32(ak[0][b], bq[1][b], sp[1]);  // keys 0..15, queries 16..31
+                sp[2] = mma32(ak[1][b], bq[1][b], sp[2]);  // keys 16..31, queries 16..31
+            }
+#pragma unroll
+            for (int i = 0; i < 3; ++i) spart[(w * 3 + i) * 64 + lane] = sp[i];
+            f4 dz[2] = {f4splat(0.0f), f4splat(0.0f)};
+#pragma unroll
+            for (int b = 0; b < PFB; ++b) {
+                const bf16x8 za = pack8t<bf16>(Z[2 * b], Z[2 * b + 1]);
+                dz[0] = mma32(za, bq[0][b], dz[0]);
+                dz[1] = mma32(za, bq[1][b], dz[1]);
+            }
+            if (g == 0) {
+                dpart[w * 32 + r] = dz[0][0];
+                dpart[w * 32 + 16 + r] = dz[1][0];
+            }
+        }
+        __syncthreads();
+
+        // ---- next chunk's tiles; scores summed over the waves
+        stage_chunk(c + 1);
+        if (threadIdx.x < 3 * 64) {
+            f4 acc = spart[threadIdx.x];
+#pragma unroll
+            for (int ww = 1; ww < 8; ++ww) acc += spart[ww * 3 * 64 + threadIdx.x];
+            stot[threadIdx.x] = acc;
+        }
+        // inter-chunk terms of both query tiles over half fh (state before
+        // this chunk), then the state update G += phi(K)^T V, z += phi(K)^T 1
+        const bf16x8 bv = kappa_col<RS>(tv, 16 * nt, lane);
+        f4 o[2] = {f4splat(0.0f), f4splat(0.0f)};
+        {
+            bf16x8 b[2][2];
+            b[0][0] = phq[(0 * NFB + GFB * fh) * 64 + lane];
+            b[0][1] = phq[(1 * NFB + GFB * fh) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < GFB; ++i) {
+                const int kb = GFB * fh + i;
+                if (i + 1 < GFB) {
+                    b[(i + 1) & 1][0] = phq[(0 * NFB + kb + 1) * 64 + lane];
+                    b[(i + 1) & 1][1] = phq[(1 * NFB + kb + 1) * 64 + lane];
+                }
+                const bf16x8 ga = pack8t<bf16>(G[2 * i], G[2 * i + 1]);
+                o[0] = mma32(ga, b[i & 1][0], o[0]);
+                o[1] = mma32(ga, b[i & 1][1], o[1]);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    G[2 * i + hf] = mma32(kappa_col<PKS>(phk, 16 * (2 * kb + hf), lane), bv, G[2 * i + hf]);
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < PFT; ++f) Z[f] = mma32(kappa_col<PKS>(phk, 16 * (PFT * w + f), lane), ones, Z[f]);
+        // the partner wave (other half, same columns) finishes the other query tile
+        xo[(ct * 2 + (1 - fh)) * 64 + lane] = fh ? o[0] : o[1];
+        __syncthreads();
+
+        // ---- outputs of query tile fh, columns 16 nt ..
+        {
+            f4 oo = (fh ? o[1] : o[0]) + xo[(ct * 2 + fh) * 64 + lane];
+            f4 s0, s1;
+            if (fh == 0) {
+                s0 = stot[0 * 64 + lane];
+                s1 = f4splat(0.0f);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g + i > r) s0[i] = 0.0f;
+            } else {
+                s0 = stot[1 * 64 + lane];
+                s1 = stot[2 * 64 + lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g + i > r) s1[i] = 0.0f;
+            }
+            const bf16x8 bs = pack8t<bf16>(s0, s1);
+            oo = mma32(bv, bs, oo);
+            const f4 di = mma32(ones, bs, f4splat(0.0f));
+            const int row = 16 * fh + r;
+            float den = di[0];
+#pragma unroll
+            for (int ww = 0; ww < 8; ++ww) den += dpart[ww * 32 + row];
+            const float inv = __builtin_amdgcn_rcpf(den);
+            const int t = t0 + row;
+            if (t < t_end) store4(out + xbase + (size_t)t * D + 16 * nt + 4 * g, oo * inv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // features: phi(x) (fp32) for 16 tokens per wave, all m features; optional
 // per-row stabiliser (two passes: the maximum, then the features).
 // ---------------------------------------------------------------------------
@@ -1509,6 +1808,18 @@ static hipError_t launch_causal_tile(const LaunchArgs& a, const bf16x8* ompack, 
     return hipGetLastError();
 }
 
+template <int M>
+static hipError_t launch_causal_wide(const LaunchArgs& a, const bf16x8* ompack, long long om_head_vecs, const bf16* q,
+                                     const bf16* k, const bf16* v, bf16* out) {
+    constexpr size_t bytes = WideSmem<M>::BYTES;
+    static_assert(bytes <= kMaxLds, "causal_wide LDS");
+    auto kern = causal_wide_kernel<M>;
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H, 2), dim3(512), bytes, a.stream, q, k, v, ompack, om_head_vecs,
+                       a.ws_carry, a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t launch_all(const LaunchArgs& a) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
@@ -1577,6 +1888,14 @@ static hipError_t launch_all(const LaunchArgs& a) {
             hipError_t err = a.m == 64    ? launch_causal_tile<64>(a, ompack, om_head_vecs, q, k, v, out)
                              : a.m == 128 ? launch_causal_tile<128>(a, ompack, om_head_vecs, q, k, v, out)
                                           : launch_causal_tile<256>(a, ompack, om_head_vecs, q, k, v, out);
+            stage_event(a, 3);
+            return err;
+        }
+    }
+    if constexpr (std::is_same<T, bf16>::value && D == 128) {
+        if (a.m == 256 || a.m == 512) {
+            hipError_t err = a.m == 256 ? launch_causal_wide<256>(a, ompack, om_head_vecs, q, k, v, out)
+                                        : launch_causal_wide<512>(a, ompack, om_head_vecs, q, k, v, out);
             stage_event(a, 3);
             return err;
         }

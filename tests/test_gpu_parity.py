@@ -140,7 +140,7 @@ def test_workload_causal_64k_sampled():
 # invariances and edge cases
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d,m", [(64, 256), (64, 128), (32, 64), (128, 128)])
+@pytest.mark.parametrize("d,m", [(64, 256), (64, 128), (32, 64), (128, 128), (128, 256), (128, 512)])
 @pytest.mark.parametrize("B,H,L", [(2, 8, 2000), (1, 16, 1411)])
 def test_causal_ragged_segments(d, m, B, H, L):
     """Segments of several chunks with a ragged last segment and a partial
@@ -224,7 +224,7 @@ def test_large_norm_stabilisers(op):
                                      (128, 256, "bidir"), (64, 512, "bidir"), (32, 160, "bidir"), (128, 512, "bidir"),
                                      (16, 32, "causal"), (32, 64, "causal"), (64, 128, "causal"), (128, 128, "causal"),
                                      (128, 256, "causal"), (64, 512, "causal"), (16, 256, "causal"), (128, 64, "causal"),
-                                     (64, 64, "causal")])
+                                     (64, 64, "causal"), (128, 512, "causal")])
 def test_other_shapes(d, m, op):
     w = WORKLOADS["causal_bf16_8k"].replace(d=d, m=m)
     inp, om, got = _run(w, op, 1, 2, 333)
