@@ -1429,9 +1429,11 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
 //     terms over half fh plus its partner's over the other half, S [V | 1],
 //     the denominator (z terms of all waves plus the row sums of S).
 // Both column halves recompute the projections (the price of keeping the
-// state in registers).  Three barriers per chunk: maxima and key features
-// ready; phi(Q), phi(K), score and denominator partials published; next
-// tiles staged, scores reduced and inter-chunk partials exchanged.
+// state in registers).  Three barriers per chunk: maxima and phi(K) rows
+// ready; phi(Q), score and denominator partials published; next tiles
+// staged, scores summed and inter-chunk partials exchanged.  Per-query
+// values of all waves (maxima, denominator terms) sit side by side, so one
+// lane reads them with two 16-byte loads.
 // ---------------------------------------------------------------------------
 template <int M>
 struct WideSmem {
@@ -1546,7 +1548,6 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
 
         // ---- projections over this wave's features
         f4 pq[2][PFT];
-        bf16x8 ak[2][PFB];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             bf16x8 x[KSD];
@@ -1568,7 +1569,7 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[tt][f][i]);
             mx = col_max(mx);
-            if (g == 0) qmax[w * 32 + 16 * tt + r] = mx;
+            if (g == 0) qmax[(16 * tt + r) * 8 + w] = mx;
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -1585,9 +1586,9 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
                 for (int ks = 0; ks < KSD; ++ks) pk[f] = mma32(om[f][ks], x[ks], pk[f]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) pk[f][i] = exp2f_fast(pk[f][i]);
+                // phi(K) row-major by token (features of tile PFT w + f)
+                lds_store4(phk + (16 * tt + r) * PKS + 16 * (PFT * w + f) + 4 * g, pk[f]);
             }
-#pragma unroll
-            for (int b = 0; b < PFB; ++b) ak[tt][b] = pack8t<bf16>(pk[2 * b], pk[2 * b + 1]);
         }
         __syncthreads();
 
@@ -1596,9 +1597,10 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
         bf16x8 bq[2][PFB];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            float mq = qmax[16 * tt + r];
-#pragma unroll
-            for (int ww = 1; ww < 8; ++ww) mq = __builtin_fmaxf(mq, qmax[ww * 32 + 16 * tt + r]);
+            const f4 m0 = *reinterpret_cast<const f4*>(qmax + (16 * tt + r) * 8);
+            const f4 m1 = *reinterpret_cast<const f4*>(qmax + (16 * tt + r) * 8 + 4);
+            const float mq = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m0[0], m0[1]), __builtin_fmaxf(m0[2], m0[3])),
+                                             __builtin_fmaxf(__builtin_fmaxf(m1[0], m1[1]), __builtin_fmaxf(m1[2], m1[3])));
 #pragma unroll
             for (int b = 0; b < PFB; ++b) {
                 f4 e0, e1;
@@ -1609,10 +1611,6 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
                 }
                 bq[tt][b] = pack8t<bf16>(e0, e1);
                 phq[(tt * NFB + PFB * w + b) * 64 + lane] = bq[tt][b];
-                const bf16x8 a = ak[tt][b];
-                bf16* row = phk + (16 * tt + r) * PKS + 16 * (PFT * w + 2 * b) + 4 * g;
-                *reinterpret_cast<bf16x4*>(row) = bf16x4{a[0], a[1], a[2], a[3]};
-                *reinterpret_cast<bf16x4*>(row + 16) = bf16x4{a[4], a[5], a[6], a[7]};
             }
         }
         {
@@ -1621,9 +1619,19 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
             for (int i = 0; i < 3; ++i) sp[i] = f4splat(0.0f);
 #pragma unroll
             for (int b = 0; b < PFB; ++b) {
-                sp[0] = mma32(ak[0][b], bq[0][b], sp[0]);  // keys 0..15, queries 0..15
-                sp[1] = mma32(ak[0][b], bq[1][b], sp[1]);  // keys 0..15, queries 16..31
-                sp[2] = mma32(ak[1][b], bq[1][b], sp[2]);  // keys 16..31, queries 16..31
+                // phi(K) of this wave's block b for keys 16 kt + r (its own
+                // rows of the phi(K) array, written before the barrier)
+                bf16x8 ak[2];
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    const bf16* pr = phk + (16 * kt + r) * PKS + 32 * (PFB * w + b) + 4 * g;
+                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(pr);
+                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(pr + 16);
+                    ak[kt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+                sp[0] = mma32(ak[0], bq[0][b], sp[0]);  // keys 0..15, queries 0..15
+                sp[1] = mma32(ak[0], bq[1][b], sp[1]);  // keys 0..15, queries 16..31
+                sp[2] = mma32(ak[1], bq[1][b], sp[2]);  // keys 16..31, queries 16..31
             }
 #pragma unroll
             for (int i = 0; i < 3; ++i) spart[(w * 3 + i) * 64 + lane] = sp[i];
@@ -1635,19 +1643,23 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
                 dz[1] = mma32(za, bq[1][b], dz[1]);
             }
             if (g == 0) {
-                dpart[w * 32 + r] = dz[0][0];
-                dpart[w * 32 + 16 + r] = dz[1][0];
+                dpart[r * 8 + w] = dz[0][0];
+                dpart[(16 + r) * 8 + w] = dz[1][0];
             }
         }
         __syncthreads();
 
         // ---- next chunk's tiles; scores summed over the waves
         stage_chunk(c + 1);
-        if (threadIdx.x < 3 * 64) {
-            f4 acc = spart[threadIdx.x];
+        {
+            const float* sps = reinterpret_cast<const float*>(spart);
+            float* sts = reinterpret_cast<float*>(stot);
+            for (int e = threadIdx.x; e < 3 * 64 * 4; e += 512) {
+                float acc = sps[e];
 #pragma unroll
-            for (int ww = 1; ww < 8; ++ww) acc += spart[ww * 3 * 64 + threadIdx.x];
-            stot[threadIdx.x] = acc;
+                for (int ww = 1; ww < 8; ++ww) acc += sps[ww * 3 * 64 * 4 + e];
+                sts[e] = acc;
+            }
         }
         // inter-chunk terms of both query tiles over half fh (state before
         // this chunk), then the state update G += phi(K)^T V, z += phi(K)^T 1
@@ -1699,9 +1711,9 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
             oo = mma32(bv, bs, oo);
             const f4 di = mma32(ones, bs, f4splat(0.0f));
             const int row = 16 * fh + r;
-            float den = di[0];
-#pragma unroll
-            for (int ww = 0; ww < 8; ++ww) den += dpart[ww * 32 + row];
+            const f4 d0 = *reinterpret_cast<const f4*>(dpart + row * 8);
+            const f4 d1 = *reinterpret_cast<const f4*>(dpart + row * 8 + 4);
+            const float den = di[0] + ((d0[0] + d0[1]) + (d0[2] + d0[3])) + ((d1[0] + d1[1]) + (d1[2] + d1[3]));
             const float inv = __builtin_amdgcn_rcpf(den);
             const int t = t0 + row;
             if (t < t_end) store4(out + xbase + (size_t)t * D + 16 * nt + 4 * g, oo * inv);
