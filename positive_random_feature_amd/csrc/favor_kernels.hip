@@ -1546,7 +1546,27 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
         const int t0 = t_begin + 32 * c;
         const bf16* tv = tv0 + (size_t)(c & 1) * SM::TILE;
 
-        // ---- projections over this wave's features
+        // ---- projections over this wave's features (keys first: their
+        // exponentials and row stores overlap the query products)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            bf16x8 x[KSD];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks)
+                x[ks] = *reinterpret_cast<const bf16x8*>(tk + (16 * tt + r) * RS + 32 * ks + 8 * g);
+            const float ck = (t0 + 16 * tt + r < t_end) ? nrm[16 * tt + r] - Mseg : kNegInf;
+            f4 pk[PFT];
+#pragma unroll
+            for (int f = 0; f < PFT; ++f) {
+                pk[f] = f4splat(ck);
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) pk[f] = mma32(om[f][ks], x[ks], pk[f]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk[f][i] = exp2f_fast(pk[f][i]);
+                // phi(K) row-major by token (features of tile PFT w + f)
+                lds_store4(phk + (16 * tt + r) * PKS + 16 * (PFT * w + f) + 4 * g, pk[f]);
+            }
+        }
         f4 pq[2][PFT];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -1570,25 +1590,6 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
                 for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[tt][f][i]);
             mx = col_max(mx);
             if (g == 0) qmax[(16 * tt + r) * 8 + w] = mx;
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            bf16x8 x[KSD];
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks)
-                x[ks] = *reinterpret_cast<const bf16x8*>(tk + (16 * tt + r) * RS + 32 * ks + 8 * g);
-            const float ck = (t0 + 16 * tt + r < t_end) ? nrm[16 * tt + r] - Mseg : kNegInf;
-            f4 pk[PFT];
-#pragma unroll
-            for (int f = 0; f < PFT; ++f) {
-                pk[f] = f4splat(ck);
-#pragma unroll
-                for (int ks = 0; ks < KSD; ++ks) pk[f] = mma32(om[f][ks], x[ks], pk[f]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pk[f][i] = exp2f_fast(pk[f][i]);
-                // phi(K) row-major by token (features of tile PFT w + f)
-                lds_store4(phk + (16 * tt + r) * PKS + 16 * (PFT * w + f) + 4 * g, pk[f]);
-            }
         }
         __syncthreads();
 
