@@ -16,7 +16,8 @@ reported under "configs" with its algorithmic work and roofline fraction.
 rocprofv3 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of this script
 (with ``--calib-copy --no-configs``) into profiles/traffic.json;
 ``python bench.py --summarise-trace TRACE_DIR`` prints per-stage launch
-times from a ``--kernel-trace`` run.
+times from a ``--kernel-trace`` run.  ``python bench.py --workload NAME``
+runs one workload alone (stage-timed calls), for profiling it.
 """
 
 from __future__ import annotations
@@ -226,6 +227,30 @@ def time_configs(hip, dev, stream, reps_target_ms: float = 20.0):
     return res
 
 
+def time_stages(hip, dev, name, calls, warmup):
+    """One workload alone: `calls` stage-timed calls after `warmup` plain ones."""
+    op = Op(name, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for _ in range(warmup):
+        op.run(stream)
+    torch.cuda.synchronize()
+    n_ev = _lib.FAVOR_N_STAGES + 1
+    evs = [[hip.event() for _ in range(n_ev)] for _ in range(calls)]
+    for i in range(calls):
+        op.run_profiled(stream, evs[i])
+    torch.cuda.synchronize()
+    per_stage = np.zeros(_lib.FAVOR_N_STAGES)
+    for i in range(calls):
+        for j in range(_lib.FAVOR_N_STAGES):
+            per_stage[j] += hip.elapsed_ms(evs[i][j], evs[i][j + 1])
+    per_stage /= calls
+    flops, bytes_ = alg_work(op.w)
+    total_s = per_stage.sum() * 1e-3
+    return {"workload": name, "calls": calls, "stage_us": [float(x * 1e3) for x in per_stage],
+            "us_per_call": total_s * 1e6, "tokens_per_s": op.w.tokens / total_s,
+            "alg_tflops": flops / total_s / 1e12, "alg_gbs": bytes_ / total_s / 1e9}
+
+
 # ---------------------------------------------------------------------------
 # Profiler summaries (rocprofv3 CSV output of runs of this script)
 # ---------------------------------------------------------------------------
@@ -330,6 +355,7 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload timings")
     ap.add_argument("--summarise-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarise-trace", metavar="TRACE_DIR")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), help="time one workload alone, stage by stage")
     args = ap.parse_args()
     if args.summarise_counters:
         summarise_counters(*args.summarise_counters)
@@ -347,6 +373,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     hip = Hip()
+    if args.workload:
+        print(json.dumps(time_stages(hip, dev, args.workload, args.steps, args.warmup)), flush=True)
+        return
     ops = [Op("bidir_bf16_4k", dev), Op("causal_bf16_8k", dev)]
     stream = torch.cuda.current_stream(dev).cuda_stream
     tokens_per_step = sum(op.w.tokens for op in ops)
