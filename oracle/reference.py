@@ -307,6 +307,49 @@ def causal(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray) -> np
     return out
 
 
+def causal_with_state(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, state=None):
+    """Causal FAVOR+ continuing from a carried prefix state, and the state
+    after the last position ([P1] Methods: G_t is a running sum over s <= t, so
+    a sequence split into pieces can hand G and z from one piece to the next;
+    [P2] Simple Derivation: the recurrent form of causal linear attention).
+
+    The state of a head is (G, z) with G = sum over the keys seen so far of
+    e(k_s) v_s^T ([m, d]) and z = sum e(k_s) ([m]), where
+    e(k)_i = exp(omega_i . k - |k|^2/2) is the feature map without its m^-1/2
+    factor.  ``state`` is None (nothing seen yet) or a pair of arrays
+    ([B, H, m, d], [B, H, m]).  Walks t = 0 .. L-1 in order: G += e(k_t) v_t^T,
+    z += e(k_t), out_t = e(q_t)^T G / e(q_t)^T z.  Returns (out [B, H, L, d],
+    (G, z)) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, L, d = q.shape
+    dv = v.shape[-1]
+    out = np.empty((B, H, L, dv), dtype=np.float64)
+    m = np.asarray(omega).shape[-2]
+    G_all = np.zeros((B, H, m, dv))
+    z_all = np.zeros((B, H, m))
+    for b in range(B):
+        for h in range(H):
+            om = _head_omega(omega, h)
+            e_q = features(q[b, h], om) * np.sqrt(m)
+            e_k = features(k[b, h], om) * np.sqrt(m)
+            if state is None:
+                G = np.zeros((m, dv))
+                z = np.zeros(m)
+            else:
+                G = np.array(state[0][b, h], dtype=np.float64)
+                z = np.array(state[1][b, h], dtype=np.float64)
+            for t in range(L):
+                G += np.outer(e_k[t], v[b, h, t])
+                z += e_k[t]
+                out[b, h, t] = (e_q[t] @ G) / (e_q[t] @ z)
+            G_all[b, h] = G
+            z_all[b, h] = z
+    return out, (G_all, z_all)
+
+
 def causal_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, rows: np.ndarray) -> np.ndarray:
     """Causal FAVOR+ output at selected positions of one head.
 

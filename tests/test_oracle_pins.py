@@ -350,3 +350,71 @@ def test_c_and_numpy_oracles_agree_multihead():
     for om in (ref.orf_omega(2, H, m, d), ref.orf_omega(2, 1, m, d)[0]):
         np.testing.assert_allclose(native.bidir(q, k, v, om), ref.bidir(q, k, v, om), rtol=1e-11, atol=1e-12)
         np.testing.assert_allclose(native.causal(q, k, v, om), ref.causal(q, k, v, om), rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# causal FAVOR+ with a carried prefix state
+# ---------------------------------------------------------------------------
+
+def _rand_qkv(rng, B, H, L, d, scale=0.5):
+    q = rng.standard_normal((B, H, L, d)) * scale
+    k = rng.standard_normal((B, H, L, d)) * scale
+    v = rng.standard_normal((B, H, L, d))
+    return q, k, v
+
+
+@pytest.mark.parametrize("split", [1, 17, 40])
+def test_causal_state_split_continues_the_recurrence(split):
+    """Two pieces with the state handed over give the single-pass causal
+    output (itself pinned to the masked L x L brute force)."""
+    rng = np.random.default_rng(11)
+    q, k, v = _rand_qkv(rng, 1, 2, 41, 8)
+    om = ref.orf_omega(3, 2, 16, 8)
+    want = ref.causal(q, k, v, om)
+    out1, st = ref.causal_with_state(q[:, :, :split], k[:, :, :split], v[:, :, :split], om)
+    out2, st2 = ref.causal_with_state(q[:, :, split:], k[:, :, split:], v[:, :, split:], om, st)
+    got = np.concatenate([out1, out2], axis=2)
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+    _, st_full = ref.causal_with_state(q, k, v, om)
+    for a, b in zip(st2, st_full):
+        assert np.allclose(a, b, rtol=1e-12, atol=0)
+
+
+def test_causal_state_empty_and_zero_match_causal():
+    rng = np.random.default_rng(12)
+    q, k, v = _rand_qkv(rng, 2, 1, 9, 4)
+    om = ref.orf_omega(5, 1, 8, 4)[0]
+    want = ref.causal(q, k, v, om)
+    out_none, _ = ref.causal_with_state(q, k, v, om)
+    out_zero, _ = ref.causal_with_state(q, k, v, om, (np.zeros((2, 1, 8, 4)), np.zeros((2, 1, 8))))
+    assert np.max(np.abs(out_none - want)) <= 1e-12 * np.max(np.abs(want))
+    assert np.max(np.abs(out_zero - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+def test_causal_state_final_state_gives_bidirectional():
+    """The state after the last position, normalised for any query, is the
+    bidirectional output for that query (all keys seen)."""
+    rng = np.random.default_rng(13)
+    q, k, v = _rand_qkv(rng, 1, 3, 23, 8)
+    om = ref.orf_omega(7, 3, 24, 8)
+    _, (G, z) = ref.causal_with_state(q, k, v, om)
+    want = ref.bidir(q, k, v, om)
+    for h in range(3):
+        e_q = np.exp(q[0, h] @ om[h].T.astype(np.float64) - 0.5 * np.sum(q[0, h] ** 2, axis=-1, keepdims=True))
+        got = (e_q @ G[0, h]) / (e_q @ z[0, h])[:, None]
+        assert np.max(np.abs(got - want[0, h])) <= 1e-12 * np.max(np.abs(want[0, h]))
+
+
+@pytest.mark.parametrize("m,d", [(4, 4), (24, 8), (7, 3)])
+def test_causal_state_scale_convention(m, d):
+    """The state carries the feature map without its m^-1/2 factor: after one
+    key k, z = e(k), and e(-k) . z = m exp(-|k|^2) for any projection (the
+    Lemma 2 limit |x + y| -> 0, [P1] Theoretical bounds)."""
+    rng = np.random.default_rng(m * 100 + d)
+    k = rng.standard_normal((1, 1, 1, d)) * 0.7
+    v = rng.standard_normal((1, 1, 1, d))
+    om = rng.standard_normal((m, d))
+    _, (_, z) = ref.causal_with_state(k, k, v, om)
+    phi_neg = ref.features(-k[0, 0, 0], om)  # m^-1/2 exp(-omega.k - |k|^2/2)
+    lhs = float(phi_neg @ z[0, 0]) / math.sqrt(m)
+    assert lhs == pytest.approx(math.exp(-float(np.sum(k ** 2))), rel=1e-12)
