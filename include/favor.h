@@ -114,6 +114,31 @@ favor_status favor_causal(const favor_shape *shape, const void *q, const void *k
                           void *stream);
 
 /*
+ * Causal FAVOR+ continuing from a carried prefix state, and the state after
+ * the last position: for streaming and autoregressive use, where a sequence
+ * arrives in pieces ("Performer" digest, Methods: G_t is a running sum over
+ * s <= t; Su Jianlin, Simple Derivation: the recurrent form).  A sequence
+ * split into pieces, each call taking the previous call's state_out as its
+ * state_in, gives the outputs of one call over the whole sequence (up to
+ * rounding).
+ * State format, per head (b, h) at offset (b H + h) (m (d + 1) + 1) floats,
+ * fp32, device memory, caller-owned:
+ *     S[m][d] row-major, then z[m], then one shift s (natural-log units),
+ * meaning G = S e^s and zsum = z e^s with
+ *     G = sum over the keys so far of e(k) v^T,  zsum = sum of e(k),
+ *     e(k)_i = exp(omega_i . k - |k|^2/2)   (the feature map without m^-1/2).
+ * state_in: NULL = no keys seen yet.  A state with S = z = 0 should be passed
+ * as NULL: its shift still takes part in the key stabiliser.
+ * state_out: NULL = not written; otherwise it receives the state including
+ * this call's keys, with one shift per head.  state_out must not overlap
+ * state_in, q, k, v, out, omega or ws (FAVOR_ERR_INVALID_ARG).  Both must be
+ * 4-byte aligned.  L = 0 writes nothing.  Other arguments as for favor_causal.
+ */
+favor_status favor_causal_state(const favor_shape *shape, const void *q, const void *k, const void *v,
+                                const float *omega, void *out, int chunk, const float *state_in,
+                                float *state_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Stage-timed variants.  Identical results to favor_bidir / favor_causal;
  * additionally, events[i] (caller-created hipEvent_t handles) is recorded on
  * `stream` before stage i and events[FAVOR_N_STAGES] after the last stage.

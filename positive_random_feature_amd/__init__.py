@@ -14,7 +14,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["features", "bidir", "causal", "orf_omega", "workspace_bytes", "FavorError"]
+__all__ = ["features", "bidir", "causal", "orf_omega", "workspace_bytes", "state_floats", "state_parts",
+           "FavorError"]
 
 FavorError = _lib.FavorError
 
@@ -100,17 +101,51 @@ def bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, omega: torch.Tensor
     return out
 
 
+def state_floats(m: int, d: int) -> int:
+    """Floats per head of a carried causal state: S [m, d], z [m], shift."""
+    return m * (d + 1) + 1
+
+
+def state_parts(state: torch.Tensor, m: int, d: int):
+    """Views (S [..., m, d], z [..., m], shift [...]) of a state tensor
+    [..., m (d + 1) + 1]; the carried sums are S e^shift and z e^shift."""
+    S = state[..., : m * d].unflatten(-1, (m, d))
+    z = state[..., m * d: m * (d + 1)]
+    return S, z, state[..., m * (d + 1)]
+
+
 def causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, omega: torch.Tensor, chunk: int = 0,
-           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Causal FAVOR+ through the prefix-sum state G_t = sum_{s<=t} phi(k_s) v_s^T."""
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+           state: torch.Tensor | None = None, return_state: bool = False):
+    """Causal FAVOR+ through the prefix-sum state G_t = sum_{s<=t} phi(k_s) v_s^T.
+
+    ``state`` ([B, H, m (d + 1) + 1] float32 on the device, or None) carries
+    the prefix of keys seen by earlier calls; with ``return_state`` the state
+    including this call's keys is returned as well: (out, state).
+    """
     dev, dt = _check_inputs([q, k, v], omega)
     shp = _shape(q, omega)
     out = torch.empty_like(q) if out is None else out
     ws = _workspace(_lib.FAVOR_OP_CAUSAL, shp, dev) if workspace is None else workspace
-    st = _lib.load().favor_causal(ctypes.byref(shp), q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(),
-                                  out.data_ptr(), int(chunk), ws.data_ptr(), ws.numel(), _stream(dev))
-    _lib.check(st, "favor_causal")
-    return out
+    lib = _lib.load()
+    if state is None and not return_state:
+        st = lib.favor_causal(ctypes.byref(shp), q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(),
+                              out.data_ptr(), int(chunk), ws.data_ptr(), ws.numel(), _stream(dev))
+        _lib.check(st, "favor_causal")
+        return out
+    B, H, _L, d = q.shape
+    n = state_floats(shp.m, d)
+    if state is not None:
+        if state.device != dev or state.dtype != torch.float32 or not state.is_contiguous() \
+                or tuple(state.shape) != (B, H, n):
+            raise ValueError(f"state must be a contiguous float32 [B, H, {n}] tensor on the same device")
+    new_state = torch.empty((B, H, n), dtype=torch.float32, device=dev) if return_state else None
+    st = lib.favor_causal_state(ctypes.byref(shp), q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(),
+                                out.data_ptr(), int(chunk), state.data_ptr() if state is not None else None,
+                                new_state.data_ptr() if new_state is not None else None, ws.data_ptr(), ws.numel(),
+                                _stream(dev))
+    _lib.check(st, "favor_causal_state")
+    return (out, new_state) if return_state else out
 
 
 def orf_omega(seed: int, n_heads: int, m: int, d: int) -> torch.Tensor:

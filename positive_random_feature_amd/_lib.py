@@ -56,6 +56,8 @@ def load() -> ctypes.CDLL:
     lib.favor_bidir.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.favor_causal.restype = ctypes.c_int
     lib.favor_causal.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    lib.favor_causal_state.restype = ctypes.c_int
+    lib.favor_causal_state.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp]
     for name, chunk in (("favor_bidir_profiled", False), ("favor_causal_profiled", True)):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int

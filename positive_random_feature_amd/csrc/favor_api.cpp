@@ -87,7 +87,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 favor_status run(int op, const favor_shape* s, const void* q, const void* k, const void* v, const float* omega,
                  void* out, float* phi, float* log_scale, int stabilize, void* ws, size_t ws_bytes, void* stream,
-                 void* const* events = nullptr) {
+                 void* const* events = nullptr, const float* state_in = nullptr, float* state_out = nullptr) {
     favor_status st = check_shape(s, op);
     if (st != FAVOR_OK) return st;
     if (s->L == 0) return FAVOR_OK;
@@ -109,6 +109,19 @@ favor_status run(int op, const favor_shape* s, const void* q, const void* k, con
     const Plan p = make_plan(op, *s);
     if (!ws || !aligned(ws, 256) || ws_bytes < p.total) return FAVOR_ERR_WORKSPACE;
     if (op != FAVOR_OP_FEATURES && overlaps(out, xbytes, ws, p.total)) return FAVOR_ERR_INVALID_ARG;
+    if (state_in || state_out) {
+        const size_t sbytes = (size_t)s->B * s->H * ((size_t)s->m * (s->d + 1) + 1) * sizeof(float);
+        if (!aligned(state_in, 4) || !aligned(state_out, 4)) return FAVOR_ERR_INVALID_ARG;
+        if (overlaps(state_in, sbytes, ws, p.total)) return FAVOR_ERR_INVALID_ARG;
+        if (state_out) {
+            const size_t obytes = (size_t)(s->omega_head_stride ? s->H : 1) * s->m * s->d * sizeof(float);
+            if (overlaps(state_out, sbytes, state_in, sbytes) || overlaps(state_out, sbytes, ws, p.total) ||
+                overlaps(state_out, sbytes, out, xbytes) || overlaps(state_out, sbytes, q, xbytes) ||
+                overlaps(state_out, sbytes, k, xbytes) || overlaps(state_out, sbytes, v, xbytes) ||
+                overlaps(state_out, sbytes, omega, obytes))
+                return FAVOR_ERR_INVALID_ARG;
+        }
+    }
 
     favor::LaunchArgs a{};
     a.op = op == FAVOR_OP_FEATURES ? favor::OpKind::Features
@@ -128,6 +141,8 @@ favor_status run(int op, const favor_shape* s, const void* q, const void* k, con
     a.ws_mmax = reinterpret_cast<float*>(base + off); off += p.mmax;
     a.ws_carry = reinterpret_cast<float*>(base + off); off += p.carry;
     a.ws_cmax = reinterpret_cast<float*>(base + off); off += p.cmax;
+    a.state_in = state_in;
+    a.state_out = state_out;
     a.stream = static_cast<hipStream_t>(stream);
     a.events = events;
     return favor::launch(a) == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
@@ -160,6 +175,15 @@ favor_status favor_causal(const favor_shape* shape, const void* q, const void* k
     if (chunk != 0 && shape && chunk != favor::causal_chunk_tokens(dtype_bytes(shape->dtype), shape->d, shape->m))
         return FAVOR_ERR_UNSUPPORTED;
     return run(FAVOR_OP_CAUSAL, shape, q, k, v, omega, out, nullptr, nullptr, 0, ws, ws_bytes, stream);
+}
+
+favor_status favor_causal_state(const favor_shape* shape, const void* q, const void* k, const void* v,
+                                const float* omega, void* out, int chunk, const float* state_in, float* state_out,
+                                void* ws, size_t ws_bytes, void* stream) {
+    if (chunk != 0 && shape && chunk != favor::causal_chunk_tokens(dtype_bytes(shape->dtype), shape->d, shape->m))
+        return FAVOR_ERR_UNSUPPORTED;
+    return run(FAVOR_OP_CAUSAL, shape, q, k, v, omega, out, nullptr, nullptr, 0, ws, ws_bytes, stream, nullptr,
+               state_in, state_out);
 }
 
 favor_status favor_bidir_profiled(const favor_shape* shape, const void* q, const void* k, const void* v,

@@ -34,6 +34,10 @@ struct LaunchArgs {
     float* ws_mmax;
     float* ws_carry;
     float* ws_cmax;
+    // causal only: carried-in and carried-out prefix state (nullptr: none);
+    // per head m (d + 1) + 1 floats, see favor_causal_state
+    const float* state_in;
+    float* state_out;
     hipStream_t stream;
     // optional stage events: events[i] before stage i, events[n_stages] after
     // the last one (nullptr: none)

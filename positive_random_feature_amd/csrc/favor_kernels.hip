@@ -440,6 +440,11 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
 // mode 1 (causal): carry[bh][s] = sum over segments s' < s, scaled to
 //   cmax[bh][s][fb] = max over s' <= s of the partial shifts (every key of
 //   segment s has exponents <= cmax + kTau), in the segment-sum layout.
+//   A carried-in state (state_in, per head: G[m][D] row-major, z[m], and a
+//   natural-log shift s, true values = stored * e^s) enters as a segment
+//   before the first, with shift s log2(e) in every block; state_out
+//   receives the inclusive total over all segments in the same format, with
+//   one shift per head (the largest block shift).
 // Both modes also pack log2(e) Omega for the block's 32 features (A-operand
 // order of the projection D[F x T]) into ompack, once per projection.
 // ---------------------------------------------------------------------------
@@ -447,7 +452,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
     const float* __restrict__ partial, const float* __restrict__ pmax, const float* __restrict__ omega, int om_per_head,
     int H, int m, int nseg, int mode, vec8<T>* __restrict__ kvpack, float* __restrict__ mmax,
-    float* __restrict__ carry, float* __restrict__ cmax, vec8<T>* __restrict__ ompack) {
+    float* __restrict__ carry, float* __restrict__ cmax, vec8<T>* __restrict__ ompack,
+    const float* __restrict__ state_in, float* __restrict__ state_out) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
     constexpr int NTV = D / 16;
     constexpr int NMT = NTV + 1;
@@ -504,8 +510,23 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
     } else {
         float* cb = carry + (size_t)bh * nseg * seg_stride;
         const bool writer = mt < NTV || r == 0;  // the z row: one lane per 4 features
+        const size_t st_stride = (size_t)m * (D + 1) + 1;
+        // this thread's piece in the row-major state: features 16 ft + 4 g + i,
+        // value column 16 mt + r (or z)
+        auto st_index = [&](int i) -> size_t {
+            const int f = 16 * ft + 4 * g + i;
+            return mt < NTV ? (size_t)f * D + 16 * mt + r : (size_t)m * D + f;
+        };
         f4 acc = f4splat(0.0f);
         float Mrun = kNegInf;
+        float Min = kNegInf;  // carried-in shift, log2 units
+        if (state_in) {
+            const float* si = state_in + (size_t)bh * st_stride;
+            Min = si[(size_t)m * (D + 1)] * kLog2e;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = si[st_index(i)];
+            Mrun = Min;
+        }
         for (int s0 = 0; s0 < nseg; s0 += NB) {
             f4 x[NB];
 #pragma unroll
@@ -528,10 +549,29 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
         if (half == 0) {
             // running maxima: thread s takes the maximum over segments <= s
             for (int s = threadIdx.x; s < nseg; s += blockDim.x) {
-                float Mr = kNegInf;
+                float Mr = Min;
                 for (int u = 0; u <= s; ++u) Mr = __builtin_fmaxf(Mr, pms[u]);
                 cmax[((size_t)bh * nseg + s) * nfb + fb] = Mr;
             }
+        }
+        if (state_out) {
+            // one shift per head: the largest over the carried-in shift and
+            // every segment shift of every block
+            __shared__ float red[64 * (D / 16 + 1)];
+            float mx = Min;
+            for (int e = threadIdx.x; e < nseg * nfb; e += blockDim.x) mx = __builtin_fmaxf(mx, pm[e]);
+            red[threadIdx.x] = mx;
+            __syncthreads();
+            float Mall = kNegInf;
+            for (int t = 0; t < (int)blockDim.x; ++t) Mall = __builtin_fmaxf(Mall, red[t]);
+            const float sc = (Mrun == kNegInf) ? 0.0f : exp2f_fast(Mrun - Mall);
+            float* so = state_out + (size_t)bh * st_stride;
+            if (writer) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) so[st_index(i)] = sc * acc[i];
+            }
+            if (threadIdx.x == 0 && fb == 0 && half == 0)
+                so[(size_t)m * (D + 1)] = (Mall == kNegInf) ? 0.0f : Mall * 0.69314718055994531f;
         }
     }
 }
@@ -1866,7 +1906,8 @@ static hipError_t launch_all(const LaunchArgs& a) {
     const int mode = a.op == OpKind::Bidir ? 0 : 1;
     hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(nfb, BH, 2), dim3(64 * (D / 16 + 1)), 0, st, a.ws_partial, a.ws_pmax,
                        a.omega, per_head, a.H, a.m, a.nseg, mode, reinterpret_cast<vec8<T>*>(a.ws_kvpack), a.ws_mmax,
-                       a.ws_carry, a.ws_cmax, ompack);
+                       a.ws_carry, a.ws_cmax, ompack, mode == 1 ? a.state_in : nullptr,
+                       mode == 1 ? a.state_out : nullptr);
     stage_event(a, 2);
     if (a.op == OpKind::Bidir) {
         constexpr int NTT = 2;

@@ -134,3 +134,27 @@ def test_orf_omega_invalid(lib):
     assert lib.favor_orf_omega(0, 1, 4, 4, None) == INVALID
     assert lib.favor_orf_omega(0, 0, 4, 4, out.ctypes.data) == INVALID
     assert lib.favor_orf_omega(0, 1, -4, 4, out.ctypes.data) == INVALID
+
+
+P_S1, P_S2 = 0x70000000, 0x78000000  # fake state buffers, far from the others
+
+
+def _causal_state(lib, s, si=P_S1, so=P_S2, chunk=0, o=P_O, ws=P_WS, nbytes=1 << 40):
+    return lib.favor_causal_state(ctypes.byref(s) if s is not None else None, P_Q, P_K, P_V, P_OM, o, chunk, si, so,
+                                  ws, nbytes, None)
+
+
+def test_causal_state_validation(lib):
+    """Carried-state arguments are checked before anything is launched."""
+    assert _causal_state(lib, None) == INVALID
+    assert _causal_state(lib, shp(), so=P_S1) == INVALID             # state_out aliases state_in
+    assert _causal_state(lib, shp(), so=P_S1 + 64) == INVALID        # ... or overlaps it
+    assert _causal_state(lib, shp(), so=P_O) == INVALID              # state_out overlaps out
+    assert _causal_state(lib, shp(), so=P_WS + 1024) == INVALID      # ... or the workspace
+    assert _causal_state(lib, shp(), si=None, so=P_Q) == INVALID     # ... or q
+    assert _causal_state(lib, shp(), si=P_WS + 1024, so=None) == INVALID  # state_in inside the workspace
+    assert _causal_state(lib, shp(), si=P_S1 + 2) == INVALID         # 4-byte alignment
+    assert _causal_state(lib, shp(), so=P_S2 + 2) == INVALID
+    assert _causal_state(lib, shp(), chunk=32) == UNSUPPORTED        # chunk as for favor_causal
+    assert _causal_state(lib, shp(), nbytes=1) == WORKSPACE
+    assert _causal_state(lib, shp(L=0), o=None, ws=None, nbytes=0) == OK  # L = 0: no-op, nothing written
