@@ -251,6 +251,44 @@ def time_stages(hip, dev, name, calls, warmup):
             "alg_tflops": flops / total_s / 1e12, "alg_gbs": bytes_ / total_s / 1e9}
 
 
+def time_streaming(hip, dev, stream, name="causal_bf16_8k", pieces=8, reps=50):
+    """The causal workload fed in `pieces` consecutive pieces, each call
+    continuing from the previous call's carried state (favor_causal_state)."""
+    op = Op(name, dev)
+    w = op.w
+    lib = _lib.load()
+    n = favor.state_floats(w.m, w.d)
+    step = (w.L + pieces - 1) // pieces
+    parts = []
+    for a in range(0, w.L, step):
+        b = min(w.L, a + step)
+        q, k, v = (t[:, :, a:b].contiguous() for t in (op.q, op.k, op.v))
+        shape = favor._shape(q, op.omega)
+        ws = torch.empty(favor.workspace_bytes(_lib.FAVOR_OP_CAUSAL, shape), dtype=torch.uint8, device=dev)
+        parts.append((shape, q, k, v, torch.empty_like(q), ws))
+    states = [torch.empty((w.B, w.H, n), dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def run_all():
+        for i, (shape, q, k, v, out, ws) in enumerate(parts):
+            sin = states[(i + 1) % 2].data_ptr() if i > 0 else None
+            st = lib.favor_causal_state(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        op.omega.data_ptr(), out.data_ptr(), 0, sin, states[i % 2].data_ptr(),
+                                        ws.data_ptr(), ws.numel(), stream)
+            _lib.check(st, "favor_causal_state")
+
+    for _ in range(3):
+        run_all()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(reps):
+        run_all()
+    hip.record(e1, stream)
+    ms = hip.elapsed_ms(e0, e1) / reps
+    return {"workload": name, "pieces": len(parts), "tokens_per_piece": step * w.B * w.H,
+            "us_per_sequence": ms * 1e3, "tokens_per_s": w.tokens / (ms * 1e-3)}
+
+
 # ---------------------------------------------------------------------------
 # Profiler summaries (rocprofv3 CSV output of runs of this script)
 # ---------------------------------------------------------------------------
@@ -464,6 +502,7 @@ def main():
     }
     if not args.no_configs:
         result["configs"] = time_configs(hip, dev, stream)
+        result["streaming"] = time_streaming(hip, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(ops)
     print(json.dumps(result), flush=True)
