@@ -128,30 +128,42 @@ class Op:
         _lib.check(st, w.op + " (profiled)")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources with comments and blank space removed, so
-    that counters stay valid across comment-only edits."""
+def _strip_comments(text: str) -> str:
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(kernel: str | None = None) -> str:
+    """Hash of kernel source with comments and blank space removed, so that
+    counters stay valid across comment-only edits.  With `kernel` (e.g.
+    "causal_tile"), only that kernel's definition (from its template line to
+    its closing brace) and the shared device header are hashed, so that edits
+    to other kernels leave its counters valid."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(os.path.join(ROOT, p)) as f:
             text = f.read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", "", text)
-        h.update(" ".join(text.split()).encode())
+        if kernel and p.endswith(".hip"):
+            i = text.index(f" {kernel}_kernel(")
+            start = text.rindex("\ntemplate", 0, i) + 1
+            end = text.index("\n}\n", i) + 3
+            text = text[start:end]
+        h.update(_strip_comments(text).encode())
     return h.hexdigest()[:16]
 
 
-def traffic_for(stage: str, src_hash: str):
+def traffic_for(stage: str):
     """HBM bytes per launch of a stage ("<workload>:<kernel>") from the
-    committed counter summary, or None when it is missing or was taken on
-    different kernel sources."""
+    committed counter summary, or None when it is missing or was taken on a
+    different source of that kernel."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     entry = t.get("stages", {}).get(stage)
-    if not entry or t.get("source_hash") != src_hash:
+    if not entry or entry.get("kernel_hash") != kernel_source_hash(stage.split(":")[1]):
         return None
     return entry.get("bytes_per_launch")
 
@@ -353,7 +365,8 @@ def summarise_counters(fetch_dir, write_dir):
         fk, fs = vals["FETCH_SIZE"][lab]
         wk, wsc = vals["WRITE_SIZE"].get(lab, (0.0, 1.0))
         b = (fk * fs + wk * wsc) * 1024.0
-        out["stages"][lab] = {"fetch_kib": fk, "write_kib": wk, "bytes_per_launch": b}
+        out["stages"][lab] = {"fetch_kib": fk, "write_kib": wk, "bytes_per_launch": b,
+                              "kernel_hash": kernel_source_hash(lab.split(":")[1])}
         lines.append(f"| {lab} | {fk:.1f} | {wk:.1f} | {b / 1e6:.2f} |")
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
@@ -493,7 +506,8 @@ def main():
                    "tokens_per_step": tokens_per_step, "causal_chunk": 64},
         "roofline": {"bound": "hbm", "kernel": kname, "op": dom_op.w.name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_for(dom, src_hash), "alg_bytes_per_launch": alg_bytes,
+                     "traffic": traffic_for(dom), "kernel_hash": kernel_source_hash(kname),
+                     "alg_bytes_per_launch": alg_bytes,
                      "avg_launch_ms": stage_ms[dom]},
         "per_op_tokens_per_s": {name: WORKLOADS[name].tokens / (ms * 1e-3) for name, ms in op_ms.items()},
         "stage_ms": stage_ms,
