@@ -41,6 +41,10 @@ Readings where the pages leave a step open:
   marginally N(0, I_d); ceil(m/d) independent blocks are stacked and the last
   is cut to the rows needed ([P1] core components and atomic insights:
   block-wise orthogonalisation when r > d; [P3] A.2: marginals preserved).
+* Generalised (ReLU) features: the pages name Performer-ReLU as FAVOR+ with
+  another kernel function ([P1] Digest; [P3] section 2) without printing its
+  map; the reading taken is phi(x)_i = m^-1/2 max(omega_i . x, 0), the same
+  projection with no |x|^2 term and no exponential.
 * Random numbers: the counter-based generator Philox4x64-10 (Salmon, Moraes,
   Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11) turned
   into uniforms with 53-bit mantissas and into normals with the Box-Muller
@@ -199,6 +203,29 @@ def features(x: np.ndarray, omega: np.ndarray) -> np.ndarray:
     return np.exp(proj - half_sq_norm) / np.sqrt(m)
 
 
+def features_relu(x: np.ndarray, omega: np.ndarray) -> np.ndarray:
+    """Generalised (ReLU) random features phi(x)_i = m**-1/2 * max(omega_i . x, 0)
+    (FAVOR+ with the ReLU kernel function; [P1] Digest, [P3] section 2).
+
+    ``x`` is [..., d], ``omega`` [m, d]; returns [..., m] in float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    omega = np.asarray(omega, dtype=np.float64)
+    m = omega.shape[-2]
+    proj = np.einsum("...d,...md->...m", x, omega) if omega.ndim > 2 else x @ omega.T
+    return np.maximum(proj, 0.0) / np.sqrt(m)
+
+
+def feature_map(kind: str):
+    """The feature map of a kind: "positive" (softmax kernel, the default) or
+    "relu"."""
+    if kind == "positive":
+        return features
+    if kind == "relu":
+        return features_relu
+    raise ValueError(f"unknown feature kind {kind!r}")
+
+
 def features_stabilized(x: np.ndarray, omega: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Features with the per-row maximum exponent taken out.
 
@@ -256,12 +283,14 @@ def _head_omega(omega: np.ndarray, h: int) -> np.ndarray:
     return omega[h]
 
 
-def bidir(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray) -> np.ndarray:
+def bidir(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, kind: str = "positive") -> np.ndarray:
     """Bidirectional FAVOR+ ([P1] key formulas and method flowchart).
 
     For each head: KV = phi(K)^T V (m x d), z = phi(K)^T 1_L (m),
     out_t = phi(q_t)^T KV / phi(q_t)^T z.  Inputs [B, H, L, d]; output float64.
+    ``kind`` selects the feature map (``feature_map``).
     """
+    features = feature_map(kind)
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -278,14 +307,16 @@ def bidir(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray) -> np.
     return out
 
 
-def causal(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray) -> np.ndarray:
+def causal(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, kind: str = "positive") -> np.ndarray:
     """Unidirectional FAVOR+ by the prefix-sum recurrence ([P1] Methods, core
     components: G_t = sum_{s<=t} phi(k_s) v_s^T; [P3] A.2 unidirectional
     attention).
 
     Walks t = 0 .. L-1 in order: G += phi(k_t) v_t^T, z += phi(k_t),
     out_t = phi(q_t)^T G / phi(q_t)^T z.  Inputs [B, H, L, d]; float64 out.
+    ``kind`` selects the feature map (``feature_map``).
     """
+    features = feature_map(kind)
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -350,7 +381,8 @@ def causal_with_state(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.nda
     return out, (G_all, z_all)
 
 
-def causal_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, rows: np.ndarray) -> np.ndarray:
+def causal_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, rows: np.ndarray,
+                kind: str = "positive") -> np.ndarray:
     """Causal FAVOR+ output at selected positions of one head.
 
     ``q, k, v`` are [L, d] for one head, ``omega`` [m, d]; for each t in
@@ -359,6 +391,7 @@ def causal_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, 
     keys (associativity, [P1] atomic insights), so that single rows of very
     long sequences can be checked without the whole prefix scan.
     """
+    features = feature_map(kind)
     om = np.asarray(omega, dtype=np.float64)
     phi_k = features(np.asarray(k, dtype=np.float64), om)
     v = np.asarray(v, dtype=np.float64)
@@ -370,8 +403,10 @@ def causal_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, 
     return res
 
 
-def bidir_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, rows: np.ndarray) -> np.ndarray:
+def bidir_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, rows: np.ndarray,
+               kind: str = "positive") -> np.ndarray:
     """Bidirectional FAVOR+ output at selected positions of one head."""
+    features = feature_map(kind)
     om = np.asarray(omega, dtype=np.float64)
     phi_k = features(np.asarray(k, dtype=np.float64), om)
     v = np.asarray(v, dtype=np.float64)
@@ -381,13 +416,15 @@ def bidir_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, r
     return (pq @ kv) / (pq @ z)[:, None]
 
 
-def brute_force(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, causal_mask: bool) -> np.ndarray:
+def brute_force(q: np.ndarray, k: np.ndarray, v: np.ndarray, omega: np.ndarray, causal_mask: bool,
+                kind: str = "positive") -> np.ndarray:
     """FAVOR+ through the explicit L x L matrix A-hat = phi(Q) phi(K)^T.
 
     out = diag(A-hat 1)^-1 A-hat V, with A-hat zeroed above the diagonal for
     the causal variant ([P3] section 2: the unidirectional form uses the
     lower-triangular part).  One head: q, k, v are [L, d].  Tiny inputs only.
     """
+    features = feature_map(kind)
     om = np.asarray(omega, dtype=np.float64)
     a_hat = features(q, om) @ features(k, om).T
     if causal_mask:

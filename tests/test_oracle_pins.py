@@ -418,3 +418,67 @@ def test_causal_state_scale_convention(m, d):
     phi_neg = ref.features(-k[0, 0, 0], om)  # m^-1/2 exp(-omega.k - |k|^2/2)
     lhs = float(phi_neg @ z[0, 0]) / math.sqrt(m)
     assert lhs == pytest.approx(math.exp(-float(np.sum(k ** 2))), rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# generalised (ReLU) features
+# ---------------------------------------------------------------------------
+
+def test_relu_features_hand_values():
+    om = np.array([[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0], [1.0, 1.0]])
+    x = np.array([2.0, -1.0])
+    want = np.array([2.0, 0.0, 0.0, 1.0]) / 2.0  # max(omega x, 0) / sqrt(4)
+    np.testing.assert_allclose(ref.features_relu(x, om), want, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("theta", [0.3, 1.2, 2.0, 2.9])
+def test_relu_features_arc_cosine_kernel(theta):
+    """With i.i.d. N(0, I) rows, E[phi(x) . phi(y)] for phi = m^-1/2 ReLU(omega . x)
+    is the first-order arc-cosine kernel |x||y| (sin t + (pi - t) cos t) / (2 pi),
+    t the angle between x and y (Cho and Saul, NIPS 2009): a closed form
+    independent of the oracle's code."""
+    d, m, R = 6, 16, 40000
+    rng = np.random.default_rng(int(theta * 100))
+    e1 = np.zeros(d); e1[0] = 1.0
+    e2 = np.zeros(d); e2[1] = 1.0
+    x = 1.3 * e1
+    y = 0.8 * (np.cos(theta) * e1 + np.sin(theta) * e2)
+    om = rng.standard_normal((R, m, d))
+    est = np.sum(ref.features_relu(x, om) * ref.features_relu(y, om), axis=-1)
+    want = np.linalg.norm(x) * np.linalg.norm(y) * (np.sin(theta) + (np.pi - theta) * np.cos(theta)) / (2 * np.pi)
+    se = est.std(ddof=1) / math.sqrt(R)
+    assert abs(est.mean() - want) <= 5 * se
+
+
+@pytest.mark.filterwarnings("ignore:invalid value encountered in divide:RuntimeWarning")
+@pytest.mark.parametrize("L,d,m", [(1, 2, 3), (17, 4, 8), (40, 8, 32)])
+def test_relu_causal_and_bidir_equal_brute_force(L, d, m):
+    """Recurrence and the explicit L x L form agree (associativity).  With few
+    features a query can have none positive: both forms then give 0/0 (NaN)
+    for that row, which the comparison treats as equal."""
+    rng = np.random.default_rng(L + 10 * d + 100 * m)
+    q, k, v = (rng.standard_normal((L, d)) for _ in range(3))
+    om = rng.standard_normal((m, d))
+    Q, K, V = (a[None, None] for a in (q, k, v))
+    np.testing.assert_allclose(ref.causal(Q, K, V, om, kind="relu")[0, 0],
+                               ref.brute_force(q, k, v, om, causal_mask=True, kind="relu"), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ref.bidir(Q, K, V, om, kind="relu")[0, 0],
+                               ref.brute_force(q, k, v, om, causal_mask=False, kind="relu"), rtol=1e-12, atol=1e-12)
+    rows = np.arange(L)
+    np.testing.assert_allclose(ref.causal_rows(q, k, v, om, rows, kind="relu"),
+                               ref.causal(Q, K, V, om, kind="relu")[0, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_relu_attention_positive_homogeneity():
+    """ReLU features are positively homogeneous, so scaling queries (per row)
+    or all keys by positive factors leaves the outputs unchanged; the
+    softmax-kernel features are not (a check that no |x|^2 or exponential
+    term is present)."""
+    rng = np.random.default_rng(21)
+    q, k, v = (rng.standard_normal((1, 1, 30, 4)) for _ in range(3))
+    om = rng.standard_normal((16, 4))
+    lam = rng.uniform(0.2, 5.0, size=(1, 1, 30, 1))
+    for fn in (ref.bidir, ref.causal):
+        base = fn(q, k, v, om, kind="relu")
+        np.testing.assert_allclose(fn(q * lam, k * 3.0, v, om, kind="relu"), base, rtol=1e-12, atol=1e-12)
+        assert not np.allclose(fn(q * lam, k * 3.0, v, om), fn(q, k, v, om), rtol=1e-6)
