@@ -27,6 +27,13 @@
  *   - Accumulation is fp32.  bf16 inputs give bf16 outputs.  There is no
  *     temperature: the library computes exp(q.k) exactly as defined; callers
  *     wanting softmax(q.k / sqrt(d)) pre-scale q and k by d^-1/4.
+ *   - Feature map: shape->feature selects the positive random features of
+ *     the softmax kernel (FAVOR+) or the generalised ReLU features
+ *     (Performer-ReLU; "Performer" digest and paperlayer.ai summary, section
+ *     2, name it without printing the map: phi_i = m^-1/2 max(omega_i . x, 0)
+ *     is the reading taken).  ReLU features need no stabiliser.  A query or
+ *     key prefix whose ReLU features are all zero has a zero normaliser: its
+ *     output is not finite, as in the exact formula.
  *   - Supported: d in {16, 32, 64, 128}; m a multiple of 32, 32 <= m <= 512
  *     (bidirectional and features), m in {32, 64, 128, 256, 512} (causal);
  *     fp32 only with d <= 64; B, H >= 1; L >= 0 (L = 0 is a no-op);
@@ -51,10 +58,16 @@ typedef enum {
     FAVOR_ERR_HIP = 4          /* a HIP launch failed (hipGetLastError after launch)   */
 } favor_status;
 
+typedef enum {
+    FAVOR_FEATURE_POSITIVE = 0, /* phi_i = m^-1/2 exp(omega_i . x - |x|^2/2): softmax kernel      */
+    FAVOR_FEATURE_RELU = 1      /* phi_i = m^-1/2 max(omega_i . x, 0): generalised ReLU kernel */
+} favor_feature;
+
 typedef struct {
     int B, H, L, d, m;           /* q, k, v, out: [B, H, L, d]; m random features        */
     favor_dtype dtype;           /* element type of q, k, v, out, x                      */
     long long omega_head_stride; /* 0: omega is [m, d]; m*d: omega is [H, m, d]          */
+    int feature;                 /* a favor_feature value; 0, the zero default: positive */
 } favor_shape;
 
 /* Operation codes for favor_workspace_bytes. */
@@ -78,6 +91,8 @@ size_t favor_workspace_bytes(int op, const favor_shape *shape, int chunk);
  * stabilize = 1: s = max_i(omega_i . x - |x|^2/2) per row, written to
  *                log_scale ([B, H, L] fp32, natural-log units), so that the
  *                unstabilised features are phi * exp(log_scale).
+ * ReLU features (shape->feature = FAVOR_FEATURE_RELU):
+ *     phi_i = m^-1/2 max(omega_i . x, 0); with stabilize, log_scale is 0.
  * The projection uses omega rounded to the input dtype (bf16 inputs: bf16
  * omega * log2(e), fp32 accumulation).  ws/ws_bytes: device workspace of at
  * least favor_workspace_bytes(FAVOR_OP_FEATURES, shape, 0) bytes, 256-byte
@@ -132,7 +147,9 @@ favor_status favor_causal(const favor_shape *shape, const void *q, const void *k
  * state_out: NULL = not written; otherwise it receives the state including
  * this call's keys, with one shift per head.  state_out must not overlap
  * state_in, q, k, v, out, omega or ws (FAVOR_ERR_INVALID_ARG).  Both must be
- * 4-byte aligned.  L = 0 writes nothing.  Other arguments as for favor_causal.
+ * 4-byte aligned.  L = 0 writes nothing.  Positive features only
+ * (FAVOR_FEATURE_RELU: FAVOR_ERR_UNSUPPORTED).  Other arguments as for
+ * favor_causal.
  */
 favor_status favor_causal_state(const favor_shape *shape, const void *q, const void *k, const void *v,
                                 const float *omega, void *out, int chunk, const float *state_in,

@@ -20,6 +20,7 @@ __all__ = ["features", "bidir", "causal", "orf_omega", "workspace_bytes", "state
 FavorError = _lib.FavorError
 
 _DTYPES = {torch.bfloat16: _lib.FAVOR_BF16, torch.float32: _lib.FAVOR_F32}
+_FEATURES = {"positive": _lib.FAVOR_FEATURE_POSITIVE, "relu": _lib.FAVOR_FEATURE_RELU}
 
 
 def _omega_stride(omega: torch.Tensor, H: int, m: int, d: int) -> int:
@@ -47,10 +48,14 @@ def _check_inputs(tensors, omega):
     return dev, dt
 
 
-def _shape(x: torch.Tensor, omega: torch.Tensor) -> _lib.FavorShape:
+def _shape(x: torch.Tensor, omega: torch.Tensor, feature: str = "positive") -> _lib.FavorShape:
+    """Shape descriptor; ``feature`` is "positive" (softmax-kernel features)
+    or "relu" (generalised ReLU features)."""
     B, H, L, d = x.shape
     m = omega.shape[-2]
-    return _lib.shape(B, H, L, d, m, _DTYPES[x.dtype], _omega_stride(omega, H, m, d))
+    if feature not in _FEATURES:
+        raise ValueError(f"feature must be one of {sorted(_FEATURES)}")
+    return _lib.shape(B, H, L, d, m, _DTYPES[x.dtype], _omega_stride(omega, H, m, d), _FEATURES[feature])
 
 
 def workspace_bytes(op: int, shp: _lib.FavorShape) -> int:
@@ -68,15 +73,16 @@ def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def features(x: torch.Tensor, omega: torch.Tensor, stabilize: bool = False):
-    """phi(x) = m^-1/2 exp(omega x - |x|^2/2) as fp32 [B, H, L, m].
+def features(x: torch.Tensor, omega: torch.Tensor, stabilize: bool = False, feature: str = "positive"):
+    """phi(x) = m^-1/2 exp(omega x - |x|^2/2) as fp32 [B, H, L, m]
+    (``feature="relu"``: m^-1/2 max(omega x, 0)).
 
     With ``stabilize`` the per-row maximum exponent s is taken out and
     returned as ``log_scale`` ([B, H, L]); phi * exp(log_scale) is the plain
-    feature map.  Returns (phi, log_scale or None).
+    feature map (0 for ReLU features).  Returns (phi, log_scale or None).
     """
     dev, _ = _check_inputs([x], omega)
-    shp = _shape(x, omega)
+    shp = _shape(x, omega, feature)
     B, H, L, _d = x.shape
     phi = torch.empty((B, H, L, shp.m), dtype=torch.float32, device=dev)
     log_scale = torch.empty((B, H, L), dtype=torch.float32, device=dev) if stabilize else None
@@ -89,10 +95,11 @@ def features(x: torch.Tensor, omega: torch.Tensor, stabilize: bool = False):
 
 
 def bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, omega: torch.Tensor,
-          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+          feature: str = "positive") -> torch.Tensor:
     """Bidirectional FAVOR+: phi(Q)(phi(K)^T V) / phi(Q)(phi(K)^T 1)."""
     dev, dt = _check_inputs([q, k, v], omega)
-    shp = _shape(q, omega)
+    shp = _shape(q, omega, feature)
     out = torch.empty_like(q) if out is None else out
     ws = _workspace(_lib.FAVOR_OP_BIDIR, shp, dev) if workspace is None else workspace
     st = _lib.load().favor_bidir(ctypes.byref(shp), q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(),
@@ -116,15 +123,16 @@ def state_parts(state: torch.Tensor, m: int, d: int):
 
 def causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, omega: torch.Tensor, chunk: int = 0,
            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-           state: torch.Tensor | None = None, return_state: bool = False):
+           state: torch.Tensor | None = None, return_state: bool = False, feature: str = "positive"):
     """Causal FAVOR+ through the prefix-sum state G_t = sum_{s<=t} phi(k_s) v_s^T.
 
     ``state`` ([B, H, m (d + 1) + 1] float32 on the device, or None) carries
     the prefix of keys seen by earlier calls; with ``return_state`` the state
     including this call's keys is returned as well: (out, state).
+    ``feature="relu"`` selects the generalised ReLU features (no carried state).
     """
     dev, dt = _check_inputs([q, k, v], omega)
-    shp = _shape(q, omega)
+    shp = _shape(q, omega, feature)
     out = torch.empty_like(q) if out is None else out
     ws = _workspace(_lib.FAVOR_OP_CAUSAL, shp, dev) if workspace is None else workspace
     lib = _lib.load()

@@ -13,6 +13,8 @@ FAVOR_OP_FEATURES = 0
 FAVOR_OP_BIDIR = 1
 FAVOR_OP_CAUSAL = 2
 FAVOR_N_STAGES = 3
+FAVOR_FEATURE_POSITIVE = 0
+FAVOR_FEATURE_RELU = 1
 
 STATUS = {0: "FAVOR_OK", 1: "FAVOR_ERR_INVALID_ARG", 2: "FAVOR_ERR_UNSUPPORTED", 3: "FAVOR_ERR_WORKSPACE",
           4: "FAVOR_ERR_HIP"}
@@ -27,6 +29,7 @@ class FavorShape(ctypes.Structure):
         ("m", ctypes.c_int),
         ("dtype", ctypes.c_int),
         ("omega_head_stride", ctypes.c_longlong),
+        ("feature", ctypes.c_int),
     ]
 
 
@@ -71,8 +74,9 @@ def load() -> ctypes.CDLL:
     return lib
 
 
-def shape(B: int, H: int, L: int, d: int, m: int, dtype: int, omega_head_stride: int) -> FavorShape:
-    return FavorShape(B, H, L, d, m, dtype, omega_head_stride)
+def shape(B: int, H: int, L: int, d: int, m: int, dtype: int, omega_head_stride: int,
+          feature: int = FAVOR_FEATURE_POSITIVE) -> FavorShape:
+    return FavorShape(B, H, L, d, m, dtype, omega_head_stride, feature)
 
 
 def check(status: int, where: str) -> None:

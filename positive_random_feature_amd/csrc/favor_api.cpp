@@ -26,6 +26,7 @@ favor_status check_shape(const favor_shape* s, int op) {
     if (!s) return FAVOR_ERR_INVALID_ARG;
     if (s->B < 1 || s->H < 1 || s->L < 0 || s->d < 1 || s->m < 1) return FAVOR_ERR_INVALID_ARG;
     if (s->dtype != FAVOR_F32 && s->dtype != FAVOR_BF16) return FAVOR_ERR_UNSUPPORTED;
+    if (s->feature != FAVOR_FEATURE_POSITIVE && s->feature != FAVOR_FEATURE_RELU) return FAVOR_ERR_UNSUPPORTED;
     if (s->d != 16 && s->d != 32 && s->d != 64 && s->d != 128) return FAVOR_ERR_UNSUPPORTED;
     if (s->m % 32 != 0 || s->m > 512) return FAVOR_ERR_UNSUPPORTED;
     if (s->m > 256 && s->m % 64 != 0) return FAVOR_ERR_UNSUPPORTED;
@@ -129,6 +130,7 @@ favor_status run(int op, const favor_shape* s, const void* q, const void* k, con
     a.dtype_bytes = eb;
     a.B = s->B; a.H = s->H; a.L = s->L; a.D = s->d; a.m = s->m;
     a.omega_per_head = s->omega_head_stride != 0;
+    a.relu = s->feature == FAVOR_FEATURE_RELU;
     a.q = q; a.k = k; a.v = v; a.omega = omega; a.out = out;
     a.phi = phi; a.log_scale = log_scale; a.stabilize = stabilize ? 1 : 0;
     a.nseg = p.nseg; a.seg_len = p.seg_len;
@@ -182,6 +184,7 @@ favor_status favor_causal_state(const favor_shape* shape, const void* q, const v
                                 void* ws, size_t ws_bytes, void* stream) {
     if (chunk != 0 && shape && chunk != favor::causal_chunk_tokens(dtype_bytes(shape->dtype), shape->d, shape->m))
         return FAVOR_ERR_UNSUPPORTED;
+    if (shape && shape->feature != FAVOR_FEATURE_POSITIVE) return FAVOR_ERR_UNSUPPORTED;
     return run(FAVOR_OP_CAUSAL, shape, q, k, v, omega, out, nullptr, nullptr, 0, ws, ws_bytes, stream, nullptr,
                state_in, state_out);
 }

@@ -184,6 +184,15 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Feature nonlinearity applied to a projected value: 2^x for the positive
+// (softmax-kernel) features, whose exponent x is already in log2 units and
+// shifted; max(x, 0) for the generalised ReLU features (x = log2(e) omega.x,
+// a constant factor that cancels in normalised attention).
+template <bool RELU> __device__ __forceinline__ float feat(float x) {
+    if constexpr (RELU) return __builtin_fmaxf(x, 0.0f);
+    else return exp2f_fast(x);
+}
+
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16

@@ -19,6 +19,7 @@ struct LaunchArgs {
     int dtype_bytes;  // 2 = bf16, 4 = fp32
     int B, H, L, D, m;
     bool omega_per_head;
+    bool relu;  // generalised ReLU features instead of the positive ones
     const void *q, *k, *v;  // for Features, q is x
     const float* omega;
     void* out;

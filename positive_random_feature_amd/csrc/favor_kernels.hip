@@ -241,7 +241,7 @@ __device__ __forceinline__ size_t seg_v_off(int ft, int nt, int lane) {
 // order, transpose reads) the B operand of the update.
 // Output: partial[bh][seg][f][0..D] (column D = sum of phi), pmax[bh][seg][f/32].
 // ---------------------------------------------------------------------------
-template <typename T, int D, int PD>
+template <typename T, int D, int PD, bool RELU>
 __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                          const float* __restrict__ omega, int om_per_head,
                                                          float* __restrict__ partial, float* __restrict__ pmax, int H,
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
         float lm = kNegInf;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            f4 init = *reinterpret_cast<const f4*>(&norms[sl][16 * tt + 4 * g]) - M;
+            f4 init = RELU ? f4splat(0.0f) : *reinterpret_cast<const f4*>(&norms[sl][16 * tt + 4 * g]) - M;
             if (!full) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -341,7 +341,9 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
     // step 0: stage, project, and take its maximum as the shift
     stage(pf[0], 0);
     __syncthreads();
-    if (active) {
+    if (active && RELU) {
+        project(0, pj[0]);  // ReLU features: no shift
+    } else if (active) {
         const float tm = wave_max_uniform(project(0, pj[0]));
         M = tm;
 #pragma unroll
@@ -371,8 +373,8 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
                         f4 e0, e1;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            e0[i] = exp2f_fast(pc[2 * ks2][ft][i]);
-                            e1[i] = exp2f_fast(pc[2 * ks2 + 1][ft][i]);
+                            e0[i] = feat<RELU>(pc[2 * ks2][ft][i]);
+                            e1[i] = feat<RELU>(pc[2 * ks2 + 1][ft][i]);
                         }
                         a[ks2][ft] = pack8t<T>(e0, e1);
                     }
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
 #pragma unroll
                     for (int ft = 0; ft < NFT; ++ft) kv[ft][NT - 1] = mma32(a[ks2][ft], ones, kv[ft][NT - 1]);
                 }
-                if (more && wave_any(lm > kTau)) {
+                if (!RELU && more && wave_any(lm > kTau)) {
                     const float tm = wave_max_uniform(lm);  // raise M by tm
                     const float sc = exp2f_fast(-tm);
 #pragma unroll
@@ -584,7 +586,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
 // shift (lane-local test; the cross-lane max only when some lane needs it),
 // exponentiate into the B operand and accumulate out^T[dims | z][T].
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool OM_LDS, bool KV_LDS, int NW>
+template <typename T, int D, bool OM_LDS, bool KV_LDS, int NW, bool RELU>
 __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict__ q, const vec8<T>* __restrict__ ompack,
                                                         long long om_head_vecs, const vec8<T>* __restrict__ kvpack,
                                                         const float* __restrict__ mmax, T* __restrict__ out, int H,
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
                 const float x = to_f(xq[tt][ks][j]);
                 ss += x * x;
             }
-        cq[tt] = -0.5f * kLog2e * col_sum(ss);
+        cq[tt] = RELU ? 0.0f : -0.5f * kLog2e * col_sum(ss);
     }
     lds_dma_wait();
     __syncthreads();
@@ -653,7 +655,7 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
     // chunk's projection is issued before the current chunk's exponentials
     auto project = [&](int fb, f4 (&pp)[NTT][2]) {
         const float mb = mmax[(size_t)bh * nfb + fb];
-        const float off = (mb == kNegInf) ? kNegInf : mb - Mstar;  // per-block key shift, <= 0
+        const float off = RELU ? 0.0f : (mb == kNegInf) ? kNegInf : mb - Mstar;  // per-block key shift, <= 0
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
@@ -669,9 +671,9 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
     };
     f4 pn[NTT][2];
     project(0, pn);
-    // the first chunk sets each query's shift to its maximum
+    // the first chunk sets each query's shift to its maximum (ReLU: none)
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
+    for (int tt = 0; tt < (RELU ? 0 : NTT); ++tt) {
         float lm = kNegInf;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -701,7 +703,7 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
                 for (int i = 0; i < 4; ++i) lm[tt] = __builtin_fmaxf(lm[tt], p[tt][hh][i]);
             need |= lm[tt] > kTau;
         }
-        if (wave_any(need)) {
+        if (!RELU && wave_any(need)) {
             // raise the shift of the queries that need it, rescaling their sums
             // and the values already projected with the old shift
 #pragma unroll
@@ -727,8 +729,8 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
             f4 e0, e1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                e0[i] = exp2f_fast(p[tt][0][i]);
-                e1[i] = exp2f_fast(p[tt][1][i]);
+                e0[i] = feat<RELU>(p[tt][0][i]);
+                e1[i] = feat<RELU>(p[tt][1][i]);
             }
             bq[tt] = pack8t<T>(e0, e1);
         }
@@ -812,7 +814,7 @@ __device__ __forceinline__ void causal_reduce(const float* part, const float* pl
     }
 }
 
-template <typename T, int D, int FW, int W, int PARTS, int PD, bool OM_REGS>
+template <typename T, int D, int FW, int W, int PARTS, int PD, bool OM_REGS, bool RELU>
 __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                               const T* __restrict__ v, const vec8<T>* __restrict__ ompack,
                                                               long long om_head_vecs, const float* __restrict__ carry,
@@ -917,7 +919,7 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
                     vec8<T> x[KSD];
 #pragma unroll
                     for (int ks = 0; ks < KSD; ++ks) x[ks] = row_operand<T, D>(qt, 16 * tt + r, ks, g);
-                    const float c = nrm[32 + 16 * tt + r];
+                    const float c = RELU ? 0.0f : nrm[32 + 16 * tt + r];
                     f4 pq[NFT];
 #pragma unroll
                     for (int ft = 0; ft < NFT; ++ft) {
@@ -930,15 +932,15 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
                     for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[ft][i]);
-                    mx = col_max(mx);
+                    mx = RELU ? 0.0f : col_max(mx);
                     sq[tt] = mx;
 #pragma unroll
                     for (int kf = 0; kf < KSF; ++kf) {
                         f4 e0, e1;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            e0[i] = exp2f_fast(pq[2 * kf][i] - mx);
-                            e1[i] = exp2f_fast(pq[2 * kf + 1][i] - mx);
+                            e0[i] = feat<RELU>(pq[2 * kf][i] - mx);
+                            e1[i] = feat<RELU>(pq[2 * kf + 1][i] - mx);
                         }
                         bq[tt][kf] = pack8t<T>(e0, e1);
                     }
@@ -950,7 +952,7 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
                     vec8<T> x[KSD];
 #pragma unroll
                     for (int ks = 0; ks < KSD; ++ks) x[ks] = row_operand<T, D>(kt, 16 * tt + r, ks, g);
-                    const float c = (t0 + 16 * tt + r < t_end) ? nrm[16 * tt + r] - M : kNegInf;
+                    const float c = (t0 + 16 * tt + r < t_end) ? (RELU ? 0.0f : nrm[16 * tt + r] - M) : kNegInf;
                     f4 pk[NFT];
 #pragma unroll
                     for (int ft = 0; ft < NFT; ++ft) {
@@ -958,7 +960,7 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
 #pragma unroll
                         for (int ks = 0; ks < KSD; ++ks) pk[ft] = mma32(om_op(ft, ks), x[ks], pk[ft]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) pk[ft][i] = exp2f_fast(pk[ft][i]);
+                        for (int i = 0; i < 4; ++i) pk[ft][i] = feat<RELU>(pk[ft][i]);
                         // phi(K) row-major by token for the state update
                         lds_store4(ptw + (16 * tt + r) * PTL::RS + 16 * ft + 4 * g, pk[ft]);
                     }
@@ -1076,7 +1078,7 @@ struct TileSmem {
     static constexpr size_t BYTES = OFF_DP + sizeof(float) * 4 * 64;
 };
 
-template <int M>
+template <int M, bool RELU>
 __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, const bf16x8* __restrict__ ompack,
                                                           long long om_head_vecs, const float* __restrict__ carry,
@@ -1202,7 +1204,7 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
             // ---- queries 16s..16s+15: projection, per-query shift, phi(Q)
             bf16x8 bq[NFB];
             {
-                const float cq = nrm[64 + 16 * s + r];
+                const float cq = RELU ? 0.0f : nrm[64 + 16 * s + r];
                 bf16x8 xq[KSD];
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks)
@@ -1227,7 +1229,7 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
 #pragma unroll
                         for (int i = 0; i < GO; ++i) oa[(gi + 1) & 1][i] = om[((gi + 1) * GO + i) * 64 + lane];
                     }
-                    if (gi * GF == NF0) {  // the first NF0 tiles are done: their maximum
+                    if (!RELU && gi * GF == NF0) {  // the first NF0 tiles are done: their maximum
 #pragma unroll
                         for (int ft = 0; ft < NF0; ++ft)
 #pragma unroll
@@ -1238,21 +1240,23 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
 #pragma unroll
                     for (int f = 0; f < GF; ++f) {
                         const int ft = gi * GF + f;
-                        pq[ft] = f4splat(ft < NF0 ? cq : cq - mx);
+                        pq[ft] = f4splat((RELU || ft < NF0) ? cq : cq - mx);
 #pragma unroll
                         for (int ks = 0; ks < KSD; ++ks) pq[ft] = mma32(oa[gi & 1][f * KSD + ks], xq[ks], pq[ft]);
                     }
                 }
-                if constexpr (NF0 == NFT) {
+                if constexpr (!RELU && NF0 == NFT) {
 #pragma unroll
                     for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[ft][i]);
                     mx = col_max(mx);
                 }
+                if constexpr (!RELU) {
 #pragma unroll
-                for (int ft = 0; ft < NF0; ++ft) pq[ft] -= mx;
-                if constexpr (NF0 < NFT) {
+                    for (int ft = 0; ft < NF0; ++ft) pq[ft] -= mx;
+                }
+                if constexpr (!RELU && NF0 < NFT) {
                     float lm = kNegInf;
 #pragma unroll
                     for (int ft = NF0; ft < NFT; ++ft)
@@ -1271,8 +1275,8 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
                     f4 e0, e1;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        e0[i] = exp2f_fast(pq[2 * kb][i]);
-                        e1[i] = exp2f_fast(pq[2 * kb + 1][i]);
+                        e0[i] = feat<RELU>(pq[2 * kb][i]);
+                        e1[i] = feat<RELU>(pq[2 * kb + 1][i]);
                     }
                     bq[kb] = pack8t<bf16>(e0, e1);
                     phq[(s * NFB + kb) * 64 + lane] = bq[kb];
@@ -1361,7 +1365,7 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const int row = 16 * tt + r;
-                    const float ck = (t0 + row < t_end) ? nrm[row] - Mseg : kNegInf;
+                    const float ck = (t0 + row < t_end) ? (RELU ? 0.0f : nrm[row] - Mseg) : kNegInf;
                     bf16x8 xk[KSD];
 #pragma unroll
                     for (int ks = 0; ks < KSD; ++ks)
@@ -1378,7 +1382,7 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
 #pragma unroll
                     for (int f = 0; f < KFT; ++f) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) pk[tt][f][i] = exp2f_fast(pk[tt][f][i]);
+                        for (int i = 0; i < 4; ++i) pk[tt][f][i] = feat<RELU>(pk[tt][f][i]);
                         lds_store4(phk + off_krow + 16 * tt * PKS + 16 * (s + 4 * f), pk[tt][f]);
                     }
             }
@@ -1495,7 +1499,7 @@ struct WideSmem {
     static constexpr size_t BYTES = OFF_XO + sizeof(f4) * (size_t)4 * 2 * 64;
 };
 
-template <int M>
+template <int M, bool RELU>
 __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, const bf16x8* __restrict__ ompack,
                                                           long long om_head_vecs, const float* __restrict__ carry,
@@ -1594,7 +1598,7 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks)
                 x[ks] = *reinterpret_cast<const bf16x8*>(tk + (16 * tt + r) * RS + 32 * ks + 8 * g);
-            const float ck = (t0 + 16 * tt + r < t_end) ? nrm[16 * tt + r] - Mseg : kNegInf;
+            const float ck = (t0 + 16 * tt + r < t_end) ? (RELU ? 0.0f : nrm[16 * tt + r] - Mseg) : kNegInf;
             f4 pk[PFT];
 #pragma unroll
             for (int f = 0; f < PFT; ++f) {
@@ -1602,7 +1606,7 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks) pk[f] = mma32(om[f][ks], x[ks], pk[f]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pk[f][i] = exp2f_fast(pk[f][i]);
+                for (int i = 0; i < 4; ++i) pk[f][i] = feat<RELU>(pk[f][i]);
                 // phi(K) row-major by token (features of tile PFT w + f)
                 lds_store4(phk + (16 * tt + r) * PKS + 16 * (PFT * w + f) + 4 * g, pk[f]);
             }
@@ -1640,15 +1644,16 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
         for (int tt = 0; tt < 2; ++tt) {
             const f4 m0 = *reinterpret_cast<const f4*>(qmax + (16 * tt + r) * 8);
             const f4 m1 = *reinterpret_cast<const f4*>(qmax + (16 * tt + r) * 8 + 4);
-            const float mq = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m0[0], m0[1]), __builtin_fmaxf(m0[2], m0[3])),
-                                             __builtin_fmaxf(__builtin_fmaxf(m1[0], m1[1]), __builtin_fmaxf(m1[2], m1[3])));
+            const float mq = RELU ? 0.0f
+                                  : __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m0[0], m0[1]), __builtin_fmaxf(m0[2], m0[3])),
+                                                    __builtin_fmaxf(__builtin_fmaxf(m1[0], m1[1]), __builtin_fmaxf(m1[2], m1[3])));
 #pragma unroll
             for (int b = 0; b < PFB; ++b) {
                 f4 e0, e1;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    e0[i] = exp2f_fast(pq[tt][2 * b][i] - mq);
-                    e1[i] = exp2f_fast(pq[tt][2 * b + 1][i] - mq);
+                    e0[i] = feat<RELU>(pq[tt][2 * b][i] - mq);
+                    e1[i] = feat<RELU>(pq[tt][2 * b + 1][i] - mq);
                 }
                 bq[tt][b] = pack8t<bf16>(e0, e1);
                 phq[(tt * NFB + PFB * w + b) * 64 + lane] = bq[tt][b];
@@ -1766,7 +1771,7 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
 // features: phi(x) (fp32) for 16 tokens per wave, all m features; optional
 // per-row stabiliser (two passes: the maximum, then the features).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool RELU>
 __global__ __launch_bounds__(256) void features_kernel(const T* __restrict__ x, const vec8<T>* __restrict__ ompack,
                                                        long long om_head_vecs, float* __restrict__ phi,
                                                        float* __restrict__ log_scale, int H, int L, int m,
@@ -1794,7 +1799,10 @@ __global__ __launch_bounds__(256) void features_kernel(const T* __restrict__ x, 
     const float c = -0.5f * kLog2e * col_sum(ss);
     const int nft = m / 16;
     float s = 0.0f;
-    if (stabilize) {
+    if (RELU) {
+        // no stabiliser for ReLU features: log_scale is 0
+        if (stabilize && ok && g == 0 && log_scale) log_scale[row] = 0.0f;
+    } else if (stabilize) {
         float mx = kNegInf;
         for (int ft = 0; ft < nft; ++ft) {
             f4 p = f4splat(c);
@@ -1806,14 +1814,16 @@ __global__ __launch_bounds__(256) void features_kernel(const T* __restrict__ x, 
         s = col_max(mx);
         if (ok && g == 0 && log_scale) log_scale[row] = s / kLog2e;
     }
-    const float off = c - s - 0.5f * __builtin_log2f((float)m);
+    const float off = RELU ? 0.0f : c - s - 0.5f * __builtin_log2f((float)m);
+    // ReLU: the packed projection carries log2(e); undo it with m^-1/2
+    const float rscale = 1.0f / (kLog2e * __builtin_sqrtf((float)m));
     for (int ft = 0; ft < nft; ++ft) {
         f4 p = f4splat(off);
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) p = mma32(omh[((size_t)ft * KSD + ks) * 64 + lane], xv[ks], p);
         f4 e;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = exp2f_fast(p[i]);
+        for (int i = 0; i < 4; ++i) e[i] = RELU ? rscale * __builtin_fmaxf(p[i], 0.0f) : exp2f_fast(p[i]);
         if (ok) store4(phi + (size_t)row * m + 16 * ft + 4 * g, e);
     }
 }
@@ -1825,7 +1835,7 @@ static inline void stage_event(const LaunchArgs& a, int i) {
     if (a.events) (void)hipEventRecord(static_cast<hipEvent_t>(a.events[i]), a.stream);
 }
 
-template <typename T, int D, int FW, int W>
+template <typename T, int D, int FW, int W, bool RELU>
 static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long long om_head_vecs, const T* q,
                                 const T* k, const T* v, T* out) {
     constexpr bool OM_REGS = FW * D <= 64 * 64;
@@ -1833,7 +1843,7 @@ static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long
     constexpr size_t two = CausalSmem<T, D, FW, W, 2>::BYTES;
     const dim3 grid(a.nseg, a.B * a.H), block(64 * W);
     if constexpr (two <= kMaxLds) {
-        auto kern = causal_chunk_kernel<T, D, FW, W, 2, PD, OM_REGS>;
+        auto kern = causal_chunk_kernel<T, D, FW, W, 2, PD, OM_REGS, RELU>;
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)two);
         hipLaunchKernelGGL(kern, grid, block, two, a.stream, q, k, v, ompack, om_head_vecs, a.ws_carry, a.ws_cmax, out,
                            a.H, a.L, a.m, a.seg_len, a.nseg);
@@ -1841,7 +1851,7 @@ static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long
         return hipErrorInvalidValue;  // rejected by argument validation before any launch
     } else {
         constexpr size_t one = CausalSmem<T, D, FW, W, 1>::BYTES;
-        auto kern = causal_chunk_kernel<T, D, FW, W, 1, PD, OM_REGS>;
+        auto kern = causal_chunk_kernel<T, D, FW, W, 1, PD, OM_REGS, RELU>;
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)one);
         hipLaunchKernelGGL(kern, grid, block, one, a.stream, q, k, v, ompack, om_head_vecs, a.ws_carry, a.ws_cmax, out,
                            a.H, a.L, a.m, a.seg_len, a.nseg);
@@ -1849,31 +1859,31 @@ static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long
     return hipGetLastError();
 }
 
-template <int M>
+template <int M, bool RELU>
 static hipError_t launch_causal_tile(const LaunchArgs& a, const bf16x8* ompack, long long om_head_vecs, const bf16* q,
                                      const bf16* k, const bf16* v, bf16* out) {
     constexpr size_t bytes = TileSmem<M>::BYTES;
     static_assert(bytes <= kMaxLds, "causal_tile LDS");
-    auto kern = causal_tile_kernel<M>;
+    auto kern = causal_tile_kernel<M, RELU>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H), dim3(512), bytes, a.stream, q, k, v, ompack, om_head_vecs,
                        a.ws_carry, a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
     return hipGetLastError();
 }
 
-template <int M>
+template <int M, bool RELU>
 static hipError_t launch_causal_wide(const LaunchArgs& a, const bf16x8* ompack, long long om_head_vecs, const bf16* q,
                                      const bf16* k, const bf16* v, bf16* out) {
     constexpr size_t bytes = WideSmem<M>::BYTES;
     static_assert(bytes <= kMaxLds, "causal_wide LDS");
-    auto kern = causal_wide_kernel<M>;
+    auto kern = causal_wide_kernel<M, RELU>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H, 2), dim3(512), bytes, a.stream, q, k, v, ompack, om_head_vecs,
                        a.ws_carry, a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool RELU>
 static hipError_t launch_all(const LaunchArgs& a) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
     const long long om_head_vecs = a.omega_per_head ? (long long)(a.m / 16) * KSD * 64 : 0;
@@ -1891,7 +1901,7 @@ static hipError_t launch_all(const LaunchArgs& a) {
         hipLaunchKernelGGL((pack_omega_kernel<T, D>), dim3(pblocks), dim3(256), 0, st, a.omega, ompack, om_heads, a.m);
         const int tiles = (a.L + 15) / 16;
         const int blocks = (tiles + 3) / 4;
-        hipLaunchKernelGGL((features_kernel<T, D>), dim3(blocks, BH), dim3(256), 0, st, q, ompack, om_head_vecs,
+        hipLaunchKernelGGL((features_kernel<T, D, RELU>), dim3(blocks, BH), dim3(256), 0, st, q, ompack, om_head_vecs,
                            a.phi, a.log_scale, a.H, a.L, a.m, a.stabilize);
         return hipGetLastError();
     }
@@ -1899,7 +1909,7 @@ static hipError_t launch_all(const LaunchArgs& a) {
     const int nfg = (a.m + 255) / 256;
     stage_event(a, 0);
     constexpr int PD_KV = D >= 128 ? 1 : 2;
-    hipLaunchKernelGGL((kv_partial_kernel<T, D, PD_KV>), dim3(a.nseg, BH, nfg), dim3(512), 0, st, k, v, a.omega, per_head,
+    hipLaunchKernelGGL((kv_partial_kernel<T, D, PD_KV, RELU>), dim3(a.nseg, BH, nfg), dim3(512), 0, st, k, v, a.omega, per_head,
                        a.ws_partial, a.ws_pmax, a.H, a.L, a.m, a.seg_len, a.nseg);
     stage_event(a, 1);
     const int nfb = a.m / 32;
@@ -1920,17 +1930,17 @@ static hipError_t launch_all(const LaunchArgs& a) {
         const size_t kv_b = sizeof(vec8<T>) * 64 * (size_t)(D / 16 + 1) * (a.m / 32);
         const vec8<T>* kvp = reinterpret_cast<const vec8<T>*>(a.ws_kvpack);
         if (om_b + kv_b <= kMaxLds) {
-            auto kern = bidir_out_kernel<T, D, true, true, NW>;
+            auto kern = bidir_out_kernel<T, D, true, true, NW, RELU>;
             (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(om_b + kv_b));
             hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), om_b + kv_b, st, q, ompack, om_head_vecs, kvp,
                                a.ws_mmax, out, a.H, a.L, a.m);
         } else if (kv_b <= kMaxLds) {
-            auto kern = bidir_out_kernel<T, D, false, true, NW>;
+            auto kern = bidir_out_kernel<T, D, false, true, NW, RELU>;
             (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kv_b);
             hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), kv_b, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,
                                out, a.H, a.L, a.m);
         } else {
-            auto kern = bidir_out_kernel<T, D, false, false, NW>;
+            auto kern = bidir_out_kernel<T, D, false, false, NW, RELU>;
             hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), 0, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,
                                out, a.H, a.L, a.m);
         }
@@ -1939,31 +1949,31 @@ static hipError_t launch_all(const LaunchArgs& a) {
     }
     if constexpr (std::is_same<T, bf16>::value && D == 64) {
         if (causal_chunk_tokens(2, D, a.m) == 64) {
-            hipError_t err = a.m == 64    ? launch_causal_tile<64>(a, ompack, om_head_vecs, q, k, v, out)
-                             : a.m == 128 ? launch_causal_tile<128>(a, ompack, om_head_vecs, q, k, v, out)
-                                          : launch_causal_tile<256>(a, ompack, om_head_vecs, q, k, v, out);
+            hipError_t err = a.m == 64    ? launch_causal_tile<64, RELU>(a, ompack, om_head_vecs, q, k, v, out)
+                             : a.m == 128 ? launch_causal_tile<128, RELU>(a, ompack, om_head_vecs, q, k, v, out)
+                                          : launch_causal_tile<256, RELU>(a, ompack, om_head_vecs, q, k, v, out);
             stage_event(a, 3);
             return err;
         }
     }
     if constexpr (std::is_same<T, bf16>::value && D == 128) {
         if (a.m == 256 || a.m == 512) {
-            hipError_t err = a.m == 256 ? launch_causal_wide<256>(a, ompack, om_head_vecs, q, k, v, out)
-                                        : launch_causal_wide<512>(a, ompack, om_head_vecs, q, k, v, out);
+            hipError_t err = a.m == 256 ? launch_causal_wide<256, RELU>(a, ompack, om_head_vecs, q, k, v, out)
+                                        : launch_causal_wide<512, RELU>(a, ompack, om_head_vecs, q, k, v, out);
             stage_event(a, 3);
             return err;
         }
     }
     const CausalCfg cfg = causal_config(D, a.m);
     hipError_t err = hipErrorInvalidValue;
-    if (cfg.fw == 32 && cfg.w == 1) err = launch_causal<T, D, 32, 1>(a, ompack, om_head_vecs, q, k, v, out);
-    else if (cfg.fw == 64 && cfg.w == 1) err = launch_causal<T, D, 64, 1>(a, ompack, om_head_vecs, q, k, v, out);
-    else if (cfg.fw == 64 && cfg.w == 2) err = launch_causal<T, D, 64, 2>(a, ompack, om_head_vecs, q, k, v, out);
-    else if (cfg.fw == 64 && cfg.w == 4) err = launch_causal<T, D, 64, 4>(a, ompack, om_head_vecs, q, k, v, out);
+    if (cfg.fw == 32 && cfg.w == 1) err = launch_causal<T, D, 32, 1, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+    else if (cfg.fw == 64 && cfg.w == 1) err = launch_causal<T, D, 64, 1, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+    else if (cfg.fw == 64 && cfg.w == 2) err = launch_causal<T, D, 64, 2, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+    else if (cfg.fw == 64 && cfg.w == 4) err = launch_causal<T, D, 64, 4, RELU>(a, ompack, om_head_vecs, q, k, v, out);
     else if constexpr (D <= 64) {
-        if (cfg.fw == 64 && cfg.w == 8) err = launch_causal<T, D, 64, 8>(a, ompack, om_head_vecs, q, k, v, out);
+        if (cfg.fw == 64 && cfg.w == 8) err = launch_causal<T, D, 64, 8, RELU>(a, ompack, om_head_vecs, q, k, v, out);
     } else {
-        if (cfg.fw == 128 && cfg.w == 4) err = launch_causal<T, D, 128, 4>(a, ompack, om_head_vecs, q, k, v, out);
+        if (cfg.fw == 128 && cfg.w == 4) err = launch_causal<T, D, 128, 4, RELU>(a, ompack, om_head_vecs, q, k, v, out);
     }
     stage_event(a, 3);
     return err;
@@ -1997,22 +2007,25 @@ size_t causal_smem_bytes(int dtype_bytes, int D, int m) {
            sizeof(float) * (size_t)c.w * 32 * (D + 4) + sizeof(float) * (size_t)c.w * 32 + sizeof(float) * 2 * 2 * 32;
 }
 
-hipError_t launch(const LaunchArgs& a) {
+template <bool RELU>
+static hipError_t launch_kind(const LaunchArgs& a) {
     if (a.dtype_bytes == 2) {
         switch (a.D) {
-            case 16: return launch_all<bf16, 16>(a);
-            case 32: return launch_all<bf16, 32>(a);
-            case 64: return launch_all<bf16, 64>(a);
-            case 128: return launch_all<bf16, 128>(a);
+            case 16: return launch_all<bf16, 16, RELU>(a);
+            case 32: return launch_all<bf16, 32, RELU>(a);
+            case 64: return launch_all<bf16, 64, RELU>(a);
+            case 128: return launch_all<bf16, 128, RELU>(a);
         }
     } else {
         switch (a.D) {
-            case 16: return launch_all<float, 16>(a);
-            case 32: return launch_all<float, 32>(a);
-            case 64: return launch_all<float, 64>(a);
+            case 16: return launch_all<float, 16, RELU>(a);
+            case 32: return launch_all<float, 32, RELU>(a);
+            case 64: return launch_all<float, 64, RELU>(a);
         }
     }
     return hipErrorInvalidValue;
 }
+
+hipError_t launch(const LaunchArgs& a) { return a.relu ? launch_kind<true>(a) : launch_kind<false>(a); }
 
 }  // namespace favor

@@ -28,8 +28,8 @@ def lib():
     return _lib.load()
 
 
-def shp(B=1, H=2, L=64, d=64, m=256, dtype=_lib.FAVOR_BF16, stride=0):
-    return _lib.shape(B, H, L, d, m, dtype, stride)
+def shp(B=1, H=2, L=64, d=64, m=256, dtype=_lib.FAVOR_BF16, stride=0, feature=_lib.FAVOR_FEATURE_POSITIVE):
+    return _lib.shape(B, H, L, d, m, dtype, stride, feature)
 
 
 def test_exports_every_declared_symbol(lib):
@@ -158,3 +158,13 @@ def test_causal_state_validation(lib):
     assert _causal_state(lib, shp(), chunk=32) == UNSUPPORTED        # chunk as for favor_causal
     assert _causal_state(lib, shp(), nbytes=1) == WORKSPACE
     assert _causal_state(lib, shp(L=0), o=None, ws=None, nbytes=0) == OK  # L = 0: no-op, nothing written
+
+
+def test_feature_kind_validation(lib):
+    assert _bidir(lib, shp(feature=2)) == UNSUPPORTED
+    assert _causal(lib, shp(feature=-1)) == UNSUPPORTED
+    assert _bidir(lib, shp(feature=_lib.FAVOR_FEATURE_RELU), nbytes=1) == WORKSPACE   # accepted up to the workspace
+    assert _causal(lib, shp(feature=_lib.FAVOR_FEATURE_RELU), nbytes=1) == WORKSPACE
+    assert _causal_state(lib, shp(feature=_lib.FAVOR_FEATURE_RELU)) == UNSUPPORTED  # no carried state for ReLU
+    # the struct the binding passes has the header's layout
+    assert ctypes.sizeof(_lib.FavorShape) == 40
