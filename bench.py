@@ -84,7 +84,7 @@ def to_dev_bf16(bits, dev):
 
 
 class Op:
-    def __init__(self, name, dev):
+    def __init__(self, name, dev, feature="positive"):
         self.w = WORKLOADS[name]
         w = self.w
         inp = make_inputs(w)
@@ -97,7 +97,7 @@ class Op:
         self.omega_host = om.numpy() if w.omega_per_head else om[0].numpy()
         self.omega = (om if w.omega_per_head else om[0]).contiguous().to(dev)
         self.out = torch.empty_like(self.q)
-        self.shape = favor._shape(self.q, self.omega)
+        self.shape = favor._shape(self.q, self.omega, feature)
         opcode = _lib.FAVOR_OP_BIDIR if w.op == "bidir" else _lib.FAVOR_OP_CAUSAL
         self.ws = torch.empty(favor.workspace_bytes(opcode, self.shape), dtype=torch.uint8, device=dev)
 
@@ -204,10 +204,14 @@ def alg_work(w):
 
 def time_configs(hip, dev, stream, reps_target_ms: float = 20.0):
     """Each workload on its own: per-call time (events around back-to-back
-    calls on one stream) and its fraction of the binding roofline."""
+    calls on one stream) and its fraction of the binding roofline; the two
+    step workloads also with the generalised ReLU features ("<name>:relu",
+    the same algorithmic work without the exponentials)."""
     res = {}
-    for name, w in WORKLOADS.items():
-        op = Op(name, dev)
+    runs = [(name, "positive") for name in WORKLOADS] + [("bidir_bf16_4k", "relu"), ("causal_bf16_8k", "relu")]
+    for name, feature in runs:
+        w = WORKLOADS[name]
+        op = Op(name, dev, feature)
         for _ in range(3):
             op.run(stream)
         torch.cuda.synchronize()
@@ -227,7 +231,8 @@ def time_configs(hip, dev, stream, reps_target_ms: float = 20.0):
         t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
         bound = "mfma" if t_mfma > t_hbm else "hbm"
         t_roof = max(t_mfma, t_hbm)
-        res[name] = {"op": w.op, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "m": w.m, "dtype": w.dtype,
+        res[name if feature == "positive" else f"{name}:{feature}"] = {
+                     "op": w.op, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "m": w.m, "dtype": w.dtype,
                      "calls": n, "us_per_call": ms * 1e3, "tokens_per_s": w.tokens / (ms * 1e-3),
                      "alg_gflop": flops / 1e9, "alg_mb": bytes_ / 1e6, "bound": bound,
                      "roof_us": t_roof * 1e6, "frac": t_roof / (ms * 1e-3),
