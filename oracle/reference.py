@@ -189,6 +189,59 @@ def orf_omega(seed: int, n_heads: int, m: int, d: int) -> np.ndarray:
 # [P2] Simple Derivation)
 # ---------------------------------------------------------------------------
 
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """Normalised Walsh-Hadamard matrix of order d (a power of two), Sylvester
+    order: H[i][j] = (-1)^popcount(i & j) / sqrt(d)."""
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    assert h.shape[0] == d, "d must be a power of two"
+    return h / np.sqrt(d)
+
+
+def hadamard_block_from_signs(signs: np.ndarray) -> np.ndarray:
+    """One structured orthogonal block sqrt(d) H S1 H S2 H S3 for sign rows
+    ``signs`` ([3, d] of +-1), S_t = diag(signs[t])."""
+    d = signs.shape[1]
+    h = sylvester_hadamard(d)
+    w = np.eye(d)
+    for t in range(3):
+        w = w @ h @ np.diag(signs[t].astype(np.float64))
+    return np.sqrt(d) * w
+
+
+def hadamard_signs(seed: int, block: int, head: int, d: int) -> np.ndarray:
+    """The +-1 diagonals of one block: diagonal t reads Philox4x64-10 with key
+    (seed, 0) and counter (0, block, head, 2 + t); entry j is -1 when bit
+    j % 64 of output word j // 64 is set (d <= 256)."""
+    assert d <= 256
+    ctr = np.array([[0, block, head, 2 + t] for t in range(3)], dtype=np.uint64)
+    w = philox4x64_10(ctr, (seed, 0))
+    j = np.arange(d)
+    bits = (w[:, j // 64] >> (j % 64).astype(np.uint64)) & np.uint64(1)
+    return np.where(bits == 1, -1.0, 1.0)
+
+
+def hadamard_omega(seed: int, n_heads: int, m: int, d: int) -> np.ndarray:
+    """Structured (Hadamard) orthogonal projection, [n_heads, m, d] float32.
+
+    The pages name Hadamard ORFs as a cheaper ORF variant with a small bias
+    that vanishes as d grows ([P3] A.2 ORF bullet and B.3 space/time
+    trade-offs) without printing a construction; the reading taken is the
+    structured block sqrt(d) H S1 H S2 H S3 (rows orthogonal, each of norm
+    sqrt(d)), ceil(m/d) independent blocks per head, the last cut to the rows
+    needed.
+    """
+    out = np.empty((n_heads, m, d), dtype=np.float32)
+    nb = (m + d - 1) // d
+    for h in range(n_heads):
+        for b in range(nb):
+            blk = hadamard_block_from_signs(hadamard_signs(seed, b, h, d))
+            rows = min(d, m - b * d)
+            out[h, b * d: b * d + rows] = blk[:rows].astype(np.float32)
+    return out
+
+
 def features(x: np.ndarray, omega: np.ndarray) -> np.ndarray:
     """phi(x)_i = m**-1/2 * exp(omega_i . x - |x|^2 / 2).
 

@@ -482,3 +482,48 @@ def test_relu_attention_positive_homogeneity():
         base = fn(q, k, v, om, kind="relu")
         np.testing.assert_allclose(fn(q * lam, k * 3.0, v, om, kind="relu"), base, rtol=1e-12, atol=1e-12)
         assert not np.allclose(fn(q * lam, k * 3.0, v, om), fn(q, k, v, om), rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# structured (Hadamard) orthogonal projections
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [1, 2, 16, 128])
+def test_sylvester_hadamard_matches_library(d):
+    import scipy.linalg
+    np.testing.assert_array_equal(ref.sylvester_hadamard(d) * np.sqrt(d), scipy.linalg.hadamard(d))
+
+
+def test_hadamard_block_structure_from_signs():
+    """All-plus signs give sqrt(d) H^3 = sqrt(d) H (H is symmetric and
+    orthogonal, so H^2 = I): a missing or extra Hadamard factor fails.  One
+    flipped sign flips the matching column."""
+    d = 16
+    h = ref.sylvester_hadamard(d)
+    ones = np.ones((3, d))
+    np.testing.assert_allclose(ref.hadamard_block_from_signs(ones), np.sqrt(d) * h, atol=1e-12)
+    s = ones.copy()
+    s[2, 5] = -1.0
+    want = np.sqrt(d) * h
+    want[:, 5] *= -1.0
+    np.testing.assert_allclose(ref.hadamard_block_from_signs(s), want, atol=1e-12)
+
+
+@pytest.mark.parametrize("m,d", [(16, 16), (40, 16), (512, 128), (96, 32)])
+def test_hadamard_omega_orthogonal_rows(m, d):
+    om = ref.hadamard_omega(3, 2, m, d).astype(np.float64)
+    for h in range(2):
+        for b in range((m + d - 1) // d):
+            blk = om[h, b * d: min(m, (b + 1) * d)]
+            g = blk @ blk.T
+            np.testing.assert_allclose(g, d * np.eye(len(blk)), atol=1e-4 * d)
+
+
+def test_hadamard_signs_balanced_and_seeded():
+    """Signs are fair coins across blocks and heads (binomial bounds), and
+    different seeds give different projections."""
+    s = np.stack([ref.hadamard_signs(7, b, h, 128) for b in range(8) for h in range(8)])
+    n = s.size
+    frac = (s > 0).mean()
+    assert abs(frac - 0.5) <= 5 * 0.5 / np.sqrt(n)
+    assert not np.array_equal(ref.hadamard_omega(1, 1, 32, 16), ref.hadamard_omega(2, 1, 32, 16))
