@@ -189,6 +189,25 @@ favor_status favor_causal_profiled(const favor_shape *shape, const void *q, cons
  */
 favor_status favor_orf_omega(unsigned long long seed, int n_heads, int m, int d, float *omega_host);
 
+/*
+ * Structured (Hadamard) orthogonal projection generated on the DEVICE:
+ * omega[n_heads, m, d] (fp32, device memory, 16-byte aligned), enqueued on
+ * `stream`.  Hadamard ORFs need only O(m) random numbers and carry a small
+ * bias that vanishes as d grows (paperlayer.ai summary, A.2 ORF bullet and
+ * B.3 trade-offs; the pages print no construction).  Each d x d block is
+ * sqrt(d) H S1 H S2 H S3, H the normalised Sylvester-Hadamard matrix
+ * (H[i][j] = (-1)^popcount(i & j) / sqrt(d)) and S_t diagonal +-1; rows are
+ * orthogonal with norm sqrt(d); ceil(m/d) independent blocks per head, the
+ * last cut to the rows needed.  Diagonal t of block b of head h takes its
+ * signs from Philox4x64-10 with key (seed, 0) and counter (0, b, h, 2 + t):
+ * entry j is -1 when bit j % 64 of output word j / 64 is set.  Values are
+ * exact in fp32.  The result is an ordinary projection for the attention
+ * entry points.  d in {16, 32, 64, 128} (else FAVOR_ERR_UNSUPPORTED); null or
+ * misaligned omega, n_heads < 1 or m < 1: FAVOR_ERR_INVALID_ARG.
+ */
+favor_status favor_hadamard_omega(unsigned long long seed, int n_heads, int m, int d, float *omega,
+                                  void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *favor_status_string(favor_status status);
 

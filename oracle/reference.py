@@ -189,25 +189,32 @@ def orf_omega(seed: int, n_heads: int, m: int, d: int) -> np.ndarray:
 # [P2] Simple Derivation)
 # ---------------------------------------------------------------------------
 
-def sylvester_hadamard(d: int) -> np.ndarray:
-    """Normalised Walsh-Hadamard matrix of order d (a power of two), Sylvester
-    order: H[i][j] = (-1)^popcount(i & j) / sqrt(d)."""
+def sylvester_hadamard_int(d: int) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard matrix of order d (a power of two),
+    Sylvester order: entries (-1)^popcount(i & j), as float64 integers."""
     h = np.ones((1, 1))
     while h.shape[0] < d:
         h = np.block([[h, h], [h, -h]])
     assert h.shape[0] == d, "d must be a power of two"
-    return h / np.sqrt(d)
+    return h
+
+
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """Normalised Walsh-Hadamard matrix H = (unnormalised) / sqrt(d)."""
+    return sylvester_hadamard_int(d) / np.sqrt(d)
 
 
 def hadamard_block_from_signs(signs: np.ndarray) -> np.ndarray:
     """One structured orthogonal block sqrt(d) H S1 H S2 H S3 for sign rows
-    ``signs`` ([3, d] of +-1), S_t = diag(signs[t])."""
+    ``signs`` ([3, d] of +-1), S_t = diag(signs[t]).  Computed exactly as
+    (1/d) Hu S1 Hu S2 Hu S3 with the integer matrix Hu = sqrt(d) H: every
+    product is an integer below 2^53 and d is a power of two."""
     d = signs.shape[1]
-    h = sylvester_hadamard(d)
+    hu = sylvester_hadamard_int(d)
     w = np.eye(d)
     for t in range(3):
-        w = w @ h @ np.diag(signs[t].astype(np.float64))
-    return np.sqrt(d) * w
+        w = w @ hu @ np.diag(signs[t].astype(np.float64))
+    return w / d
 
 
 def hadamard_signs(seed: int, block: int, head: int, d: int) -> np.ndarray:

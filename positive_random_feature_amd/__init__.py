@@ -14,8 +14,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["features", "bidir", "causal", "orf_omega", "workspace_bytes", "state_floats", "state_parts",
-           "FavorError"]
+__all__ = ["features", "bidir", "causal", "orf_omega", "hadamard_omega", "workspace_bytes", "state_floats",
+           "state_parts", "FavorError"]
 
 FavorError = _lib.FavorError
 
@@ -161,4 +161,15 @@ def orf_omega(seed: int, n_heads: int, m: int, d: int) -> torch.Tensor:
     out = torch.empty((n_heads, m, d), dtype=torch.float32)
     st = _lib.load().favor_orf_omega(int(seed), int(n_heads), int(m), int(d), out.data_ptr())
     _lib.check(st, "favor_orf_omega")
+    return out
+
+
+def hadamard_omega(seed: int, n_heads: int, m: int, d: int, device="cuda") -> torch.Tensor:
+    """Structured (Hadamard) orthogonal projection [n_heads, m, d] (float32),
+    generated on the device: blocks sqrt(d) H S1 H S2 H S3 with seeded +-1
+    diagonals S_t."""
+    dev = torch.device(device)
+    out = torch.empty((n_heads, m, d), dtype=torch.float32, device=dev)
+    st = _lib.load().favor_hadamard_omega(int(seed), int(n_heads), int(m), int(d), out.data_ptr(), _stream(dev))
+    _lib.check(st, "favor_hadamard_omega")
     return out

@@ -1,0 +1,109 @@
+// Structured (Hadamard) orthogonal random projections generated on the
+// device (favor_hadamard_omega in include/favor.h).
+//
+// paperlayer.ai summary of arXiv:2009.14794v4, A.2 (ORF bullet) and B.3
+// (space and time trade-offs): Hadamard ORFs are orthogonal random features
+// that need only O(m) random numbers, at the price of a small bias that
+// vanishes as d grows.  Each d x d block here is sqrt(d) H S1 H S2 H S3,
+// with H the normalised Sylvester-Hadamard matrix and S_t diagonal +-1
+// matrices; its rows are orthogonal with norm sqrt(d).  The projection is
+// materialised ([H, m, d] fp32) and used by the matrix-core projection like
+// any other: on gfx950 a dense 16x16x32 product costs less than a fast
+// Walsh-Hadamard transform in vector instructions for d <= 128.
+//
+// Signs: Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, SC'11), key
+// (seed, 0); diagonal t of block b of head h reads counter (0, b, h, 2 + t),
+// entry j is -1 when bit j % 64 of output word j / 64 is set.
+#include "../../include/favor.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+struct Words {
+    uint64_t w[4];
+};
+
+__device__ Words philox4x64_10(Words c, uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ULL, M1 = 0xCA5A826395121157ULL;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ULL, W1 = 0xBB67AE8584CAA73BULL;
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint64_t hi0 = __umul64hi(M0, c.w[0]), lo0 = M0 * c.w[0];
+        const uint64_t hi1 = __umul64hi(M1, c.w[2]), lo1 = M1 * c.w[2];
+        Words n;
+        n.w[0] = hi1 ^ c.w[1] ^ k0;
+        n.w[1] = lo1;
+        n.w[2] = hi0 ^ c.w[3] ^ k1;
+        n.w[3] = lo0;
+        c = n;
+    }
+    return c;
+}
+
+// Unnormalised Walsh-Hadamard transform of a row vector, in place (the
+// Sylvester matrix is symmetric, so v H = H v).
+template <int D>
+__device__ __forceinline__ void fwht(float (&v)[D]) {
+#pragma unroll
+    for (int len = 1; len < D; len <<= 1)
+#pragma unroll
+        for (int i = 0; i < D; i += 2 * len)
+#pragma unroll
+            for (int j = 0; j < len; ++j) {
+                const float a = v[i + j], b = v[i + j + len];
+                v[i + j] = a + b;
+                v[i + j + len] = a - b;
+            }
+}
+
+// One thread per (head, row): row i of block b is e_i^T sqrt(d) H S1 H S2 H S3,
+// built from the unnormalised matrix Hu = sqrt(d) H as (1/d) e_i^T Hu S1 Hu S2 Hu S3.
+// Every intermediate is an integer of magnitude <= d^3, so the result is
+// exact in fp32.
+template <int D>
+__global__ __launch_bounds__(64) void hadamard_omega_kernel(unsigned long long seed, int n_heads, int m,
+                                                            float* __restrict__ omega) {
+    const long long idx = (long long)blockIdx.x * 64 + threadIdx.x;
+    if (idx >= (long long)n_heads * m) return;
+    const int h = (int)(idx / m), row = (int)(idx % m);
+    const int b = row / D, i = row % D;
+    float v[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) v[j] = (__popc(i & j) & 1) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        const Words w = philox4x64_10(Words{{0, (uint64_t)b, (uint64_t)h, (uint64_t)(2 + t)}}, seed, 0);
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if ((w.w[j / 64] >> (j % 64)) & 1) v[j] = -v[j];
+        if (t < 2) fwht<D>(v);
+    }
+    float* dst = omega + (size_t)idx * D;
+#pragma unroll
+    for (int j = 0; j < D; j += 4)
+        *reinterpret_cast<float4*>(dst + j) = float4{v[j] / D, v[j + 1] / D, v[j + 2] / D, v[j + 3] / D};
+}
+
+}  // namespace
+
+extern "C" favor_status favor_hadamard_omega(unsigned long long seed, int n_heads, int m, int d, float* omega,
+                                             void* stream) {
+    if (!omega || ((uintptr_t)omega % 16) != 0 || n_heads < 1 || m < 1) return FAVOR_ERR_INVALID_ARG;
+    if (d != 16 && d != 32 && d != 64 && d != 128) return FAVOR_ERR_UNSUPPORTED;
+    if ((long long)n_heads * m * d >= (1LL << 31)) return FAVOR_ERR_UNSUPPORTED;
+    const long long rows = (long long)n_heads * m;
+    const dim3 grid((unsigned)((rows + 63) / 64));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (d) {
+        case 16: hipLaunchKernelGGL(hadamard_omega_kernel<16>, grid, dim3(64), 0, st, seed, n_heads, m, omega); break;
+        case 32: hipLaunchKernelGGL(hadamard_omega_kernel<32>, grid, dim3(64), 0, st, seed, n_heads, m, omega); break;
+        case 64: hipLaunchKernelGGL(hadamard_omega_kernel<64>, grid, dim3(64), 0, st, seed, n_heads, m, omega); break;
+        default: hipLaunchKernelGGL(hadamard_omega_kernel<128>, grid, dim3(64), 0, st, seed, n_heads, m, omega); break;
+    }
+    return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}

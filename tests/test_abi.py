@@ -168,3 +168,13 @@ def test_feature_kind_validation(lib):
     assert _causal_state(lib, shp(feature=_lib.FAVOR_FEATURE_RELU)) == UNSUPPORTED  # no carried state for ReLU
     # the struct the binding passes has the header's layout
     assert ctypes.sizeof(_lib.FavorShape) == 40
+
+
+def test_hadamard_omega_validation(lib):
+    f = lib.favor_hadamard_omega
+    assert f(0, 1, 32, 16, None, None) == INVALID
+    assert f(0, 1, 32, 16, P_OM + 4, None) == INVALID    # 16-byte alignment
+    assert f(0, 0, 32, 16, P_OM, None) == INVALID
+    assert f(0, 1, 0, 16, P_OM, None) == INVALID
+    assert f(0, 1, 32, 48, P_OM, None) == UNSUPPORTED   # d must be 16, 32, 64 or 128
+    assert f(0, 1 << 12, 1 << 12, 128, P_OM, None) == UNSUPPORTED  # >= 2^31 elements
