@@ -268,6 +268,23 @@ def time_stages(hip, dev, name, calls, warmup):
             "alg_tflops": flops / total_s / 1e12, "alg_gbs": bytes_ / total_s / 1e9}
 
 
+def time_hadamard(hip, dev, stream, n_heads=16, m=512, d=128, reps=50):
+    """Device generation of a structured (Hadamard) projection of the long
+    causal workload's size."""
+    lib = _lib.load()
+    out = torch.empty((n_heads, m, d), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        _lib.check(lib.favor_hadamard_omega(1, n_heads, m, d, out.data_ptr(), stream), "favor_hadamard_omega")
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for i in range(reps):
+        _lib.check(lib.favor_hadamard_omega(i, n_heads, m, d, out.data_ptr(), stream), "favor_hadamard_omega")
+    hip.record(e1, stream)
+    us = hip.elapsed_ms(e0, e1) / reps * 1e3
+    return {"heads": n_heads, "m": m, "d": d, "us_per_call": us, "gbs_written": n_heads * m * d * 4 / (us * 1e-6) / 1e9}
+
+
 def time_streaming(hip, dev, stream, name="causal_bf16_8k", pieces=8, reps=50):
     """The causal workload fed in `pieces` consecutive pieces, each call
     continuing from the previous call's carried state (favor_causal_state)."""
@@ -522,6 +539,7 @@ def main():
     if not args.no_configs:
         result["configs"] = time_configs(hip, dev, stream)
         result["streaming"] = time_streaming(hip, dev, stream)
+        result["hadamard_projection"] = time_hadamard(hip, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(ops)
     print(json.dumps(result), flush=True)
