@@ -55,8 +55,11 @@ Plan make_plan(int op, const favor_shape& s) {
     const int nfg = (m + 255) / 256;  // feature groups of the partial pass
     // one partial-pass (bidirectional) or chunk-scan (causal) workgroup per
     // compute unit
-    int nseg = op == FAVOR_OP_BIDIR ? (kTargetWorkgroups + BH * nfg - 1) / (BH * nfg)
-                                    : (kTargetWorkgroups + BH - 1) / BH;
+    // the causal scan for bf16, d = 128 (m = 256, 512) runs two workgroups per
+    // (segment, head), one per half of the value columns
+    const bool wide = op == FAVOR_OP_CAUSAL && s.dtype == FAVOR_BF16 && D == 128 && (m == 256 || m == 512);
+    const int per_seg = op == FAVOR_OP_BIDIR ? BH * nfg : BH * (wide ? 2 : 1);
+    int nseg = (kTargetWorkgroups + per_seg - 1) / per_seg;
     if (nseg < 1) nseg = 1;
     if (nseg > tiles) nseg = tiles;
     const int per = (s.L + nseg - 1) / nseg;
