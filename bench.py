@@ -153,6 +153,13 @@ def kernel_source_hash(kernel: str | None = None) -> str:
     return h.hexdigest()[:16]
 
 
+def traffic_kernel_hash(kernel: str):
+    try:
+        return kernel_source_hash(kernel)
+    except ValueError:
+        return None
+
+
 def traffic_for(stage: str):
     """HBM bytes per launch of a stage ("<workload>:<kernel>") from the
     committed counter summary, or None when it is missing or was taken on a
@@ -163,7 +170,11 @@ def traffic_for(stage: str):
     with open(path) as f:
         t = json.load(f)
     entry = t.get("stages", {}).get(stage)
-    if not entry or entry.get("kernel_hash") != kernel_source_hash(stage.split(":")[1]):
+    try:
+        current = kernel_source_hash(stage.split(":")[1])
+    except ValueError:  # kernel not found in the sources
+        return None
+    if not entry or entry.get("kernel_hash") != current:
         return None
     return entry.get("bytes_per_launch")
 
@@ -528,7 +539,7 @@ def main():
                    "tokens_per_step": tokens_per_step, "causal_chunk": 64},
         "roofline": {"bound": "hbm", "kernel": kname, "op": dom_op.w.name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_for(dom), "kernel_hash": kernel_source_hash(kname),
+                     "traffic": traffic_for(dom), "kernel_hash": traffic_kernel_hash(kname),
                      "alg_bytes_per_launch": alg_bytes,
                      "avg_launch_ms": stage_ms[dom]},
         "per_op_tokens_per_s": {name: WORKLOADS[name].tokens / (ms * 1e-3) for name, ms in op_ms.items()},
