@@ -47,7 +47,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 # kernels of the three stages of each op at the bench shapes (d=64, m=256)
 STAGES = {"bidir": ["kv_partial", "merge_scan", "bidir_out"],
           "causal": ["kv_partial", "merge_scan", "causal_tile"]}
-KERNEL_SOURCES = ["positive_random_feature_amd/csrc/favor_kernels.hip", "positive_random_feature_amd/csrc/favor_device.h"]
+KERNEL_SOURCES = ["positive_random_feature_amd/csrc/favor_kernels.hip", "positive_random_feature_amd/csrc/favor_device.h",
+                  "positive_random_feature_amd/csrc/favor_api.cpp"]
 
 
 class Hip:
@@ -137,18 +138,26 @@ def _strip_comments(text: str) -> str:
 def kernel_source_hash(kernel: str | None = None) -> str:
     """Hash of kernel source with comments and blank space removed, so that
     counters stay valid across comment-only edits.  With `kernel` (e.g.
-    "causal_tile"), only that kernel's definition (from its template line to
-    its closing brace) and the shared device header are hashed, so that edits
-    to other kernels leave its counters valid."""
+    "causal_tile"), the kernel file is hashed without the definitions of the
+    other kernels (its own definition, the shared helpers and the launchers
+    stay in), together with the device header and the launch plan, so that
+    edits to other kernels leave its counters valid."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(os.path.join(ROOT, p)) as f:
             text = f.read()
         if kernel and p.endswith(".hip"):
-            i = text.index(f" {kernel}_kernel(")
-            start = text.rindex("\ntemplate", 0, i) + 1
-            end = text.index("\n}\n", i) + 3
-            text = text[start:end]
+            if f" {kernel}_kernel(" not in text:
+                raise ValueError(kernel)
+            spans = []
+            for m in re.finditer(r"__global__[^\n]*?void (\w+)_kernel\(", text):
+                if m.group(1) == kernel:
+                    continue
+                start = text.rindex("\ntemplate", 0, m.start()) + 1
+                end = text.index("\n}\n", m.start()) + 3
+                spans.append((start, end))
+            for start, end in reversed(spans):
+                text = text[:start] + text[end:]
         h.update(_strip_comments(text).encode())
     return h.hexdigest()[:16]
 

@@ -107,7 +107,9 @@ __device__ __forceinline__ bf16x8 kappa_col_at(const bf16* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile prefetch: NTEN tensors, each a ROWS-row tile of D columns, split into
+// Tile prefetch by NTHR threads (thread index taken modulo NTHR, so the
+// group can be any aligned block of NTHR threads): NTEN tensors, each a
+// ROWS-row tile of D columns, split into
 // 8-element chunks (chunk c of a tensor = row c / (D/8), columns 8 (c % (D/8))).
 // load() issues global loads into registers; store() writes them to LDS
 // tiles and, for the tensors in `norm_mask`, the row constants
@@ -130,9 +132,9 @@ struct Prefetch {
     __device__ __forceinline__ static void where(int i, int& tn, int& cc) {
         if constexpr (CH % NTHR == 0) {
             tn = (i * NTHR) / CH;
-            cc = (i * NTHR) % CH + (int)threadIdx.x;
+            cc = (i * NTHR) % CH + (int)(threadIdx.x % NTHR);
         } else {
-            int c = threadIdx.x + i * NTHR;
+            int c = (int)(threadIdx.x % NTHR) + i * NTHR;
             if (TOT % NTHR != 0) c = min(c, TOT - 1);
             tn = c / CH;
             cc = c % CH;
@@ -162,7 +164,7 @@ struct Prefetch {
         constexpr int RS = LdsTile<T, D>::RS;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int c = threadIdx.x + i * NTHR;
+            const int c = (int)(threadIdx.x % NTHR) + i * NTHR;
             if (TOT % NTHR == 0 || c < TOT) {
                 int tn, cc;
                 where(i, tn, cc);
@@ -1104,7 +1106,10 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
     // and skip their matrix instructions
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s = w & 3;       // token tile and value-column tile of this wave
-    const bool qwave = w < 4;  // query wave (else key/state wave)
+    // query waves 4..7, key/state waves 0..3: the key/state waves carry the
+    // longer path in both phases and, as the older wave of each SIMD, win
+    // its instruction arbitration
+    const bool qwave = w >= 4;
     const int seg = blockIdx.x, bh = blockIdx.y, h = bh % H;
     const int t_begin = seg * seg_len;
     const int t_end = min(L, t_begin + seg_len);
