@@ -297,3 +297,35 @@ def test_features_opposite_identity(name):
     want = np.exp(-np.sum(inp.q.astype(np.float64) ** 2, axis=-1))
     err = _rel(got, want)
     assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("d,m", [(64, 256), (128, 512), (32, 64)])
+@pytest.mark.parametrize("op", ["bidir", "causal"])
+def test_injected_key_spike(d, m, op):
+    """One key deep inside the sequence aligned with a feature direction, so
+    that its exponent exceeds every earlier one by ~20 in natural-log units:
+    the segment pass must raise its key shift mid-segment, and every later
+    causal segment starts from a much larger carried-in shift.  The queries
+    aligned with that feature then attend almost only to it."""
+    w = WORKLOADS["causal_bf16_8k"].replace(d=d, m=m)
+    B, H, L = 1, 2, 3000
+    inp = make_inputs(w, B=B, H=H, L=L, seed=4)
+    om = _omega(w, H)
+    q, k, v = inp.q.copy(), inp.k.copy(), inp.v.copy()
+    for h in range(H):
+        u = om[h, 5] / np.linalg.norm(om[h, 5])
+        k[0, h, 1700] = 3.0 * u                   # exponent ~ 3|omega| - 4.5
+        q[0, h, 2500:2510] = 1.0 * u              # queries that see it
+    from positive_random_feature_amd.workloads import f32_to_bf16_bits
+    bits = [f32_to_bf16_bits(a) for a in (q, k, v)]
+    vals = [(b.astype(np.uint32) << 16).view(np.float32) for b in bits]
+    dev = [torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(_dev()) for b in bits]
+    fn = favor.bidir if op == "bidir" else favor.causal
+    got = fn(*dev, torch.from_numpy(om).to(_dev()))
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy().astype(np.float64)
+    want = (native.bidir if op == "bidir" else native.causal)(*vals, om)
+    assert np.isfinite(got).all()
+    err = _rel(got, want)
+    _log(f"key spike {op} d={d} m={m}", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
