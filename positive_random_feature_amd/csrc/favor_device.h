@@ -83,6 +83,25 @@ template <typename T> __device__ __forceinline__ vec8<T> zero8() { return splat8
 
 template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
 
+// Sum of squares of 8 elements: bf16 pairs through v_dot2c_f32_bf16 (the
+// products of bf16 values are exact in fp32), fp32 through fused multiply-adds.
+__device__ __forceinline__ float sumsq8(bf16x8 x) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+        const bf16x2 p{x[j], x[j + 1]};
+        s = __builtin_amdgcn_fdot2_f32_bf16(p, p, s, false);
+    }
+    return s;
+}
+__device__ __forceinline__ float sumsq8(f8 x) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += x[j] * x[j];
+    return s;
+}
+
 // 8 consecutive elements from global memory (16 B for bf16, 32 B for fp32).
 __device__ __forceinline__ bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ f8 load8(const float* p) {

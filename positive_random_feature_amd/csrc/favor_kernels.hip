@@ -180,12 +180,7 @@ struct Prefetch {
                 if constexpr (SWZ) off = swz_tile(row, col);
                 *reinterpret_cast<vec8<T>*>(d + off) = x;
                 if ((norm_mask >> tn) & 1) {
-                    float ss = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float xf = to_f(x[j]);
-                        ss += xf * xf;
-                    }
+                    float ss = sumsq8(x);
                     ss = group_sum<CPR>(ss);
                     if (col == 0) nrm[tn * ROWS + row] = -0.5f * kLog2e * ss;
                 }
@@ -630,12 +625,7 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
     for (int tt = 0; tt < NTT; ++tt) {
         float ss = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float x = to_f(xq[tt][ks][j]);
-                ss += x * x;
-            }
+        for (int ks = 0; ks < KSD; ++ks) ss += sumsq8(xq[tt][ks]);
         cq[tt] = RELU ? 0.0f : -0.5f * kLog2e * col_sum(ss);
     }
     lds_dma_wait();
