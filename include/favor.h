@@ -34,10 +34,11 @@
  *     is the reading taken).  ReLU features need no stabiliser.  A query or
  *     key prefix whose ReLU features are all zero has a zero normaliser: its
  *     output is not finite, as in the exact formula.
- *   - Supported: d in {16, 32, 64, 128}; m a multiple of 32, 32 <= m <= 512
- *     (bidirectional and features), m in {32, 64, 128, 256, 512} (causal);
- *     fp32 only with d <= 64; B, H >= 1; L >= 0 (L = 0 is a no-op);
- *     B*H*L*d < 2^31.
+ *   - Supported: d in {16, 32, 64, 128}; fp32 only with d <= 64;
+ *     bidirectional and features: m a multiple of 32 up to 256, or a
+ *     multiple of 64 up to 512; causal: m in {32, 64, 128, 256, 512}, except
+ *     fp32 with d = 64 and m = 512 (its scan's tiles exceed the LDS);
+ *     B, H >= 1; L >= 0 (L = 0 is a no-op); B*H*L*d < 2^31.
  */
 #ifndef FAVOR_H_
 #define FAVOR_H_

@@ -93,6 +93,28 @@ def test_validation(lib, fn):
     assert fn(lib, shp(B=1 << 16, H=1 << 8, L=1 << 8, d=64)) == UNSUPPORTED            # > 2^31 elements
 
 
+def documented_support(dtype, d, m, op):
+    """The supported set as include/favor.h states it."""
+    if d not in (16, 32, 64, 128) or (dtype == _lib.FAVOR_F32 and d > 64):
+        return False
+    if op == 2:
+        return m in (32, 64, 128, 256, 512) and not (dtype == _lib.FAVOR_F32 and d == 64 and m == 512)
+    return m >= 32 and ((m <= 256 and m % 32 == 0) or (m <= 512 and m % 64 == 0))
+
+
+def test_support_matrix_matches_header(lib):
+    # every (dtype, d, m, op) over a grid wider than the supported set: the
+    # library accepts (nonzero workspace) exactly what the header documents
+    for dtype in (_lib.FAVOR_F32, _lib.FAVOR_BF16):
+        for d in (8, 16, 24, 32, 48, 64, 96, 128, 256):
+            for m in range(16, 577, 16):
+                for op in (0, 1, 2):
+                    for feature in (_lib.FAVOR_FEATURE_POSITIVE, _lib.FAVOR_FEATURE_RELU):
+                        s = shp(d=d, m=m, dtype=dtype, feature=feature)
+                        got = lib.favor_workspace_bytes(op, ctypes.byref(s), 0) > 0
+                        assert got == documented_support(dtype, d, m, op), (dtype, d, m, op, feature)
+
+
 def test_causal_chunk_and_lds_limits(lib):
     # A one-byte workspace makes an accepted shape stop at the workspace
     # check (WORKSPACE), before anything is launched.

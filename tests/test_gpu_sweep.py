@@ -1,0 +1,89 @@
+"""GPU parity over a seeded random sweep of the supported shapes.
+
+Each case draws the input dtype, head size d, feature count m, operation
+(bidirectional or causal), feature map (positive or ReLU), batch, heads, a
+ragged sequence length and whether the projection is shared or per head, and
+compares every output element with the fp64 oracle.  The draws reach every
+launch plan of the library (the 64-token tile scan, the two-workgroup d = 128
+scan and the generic chunk scan for causal attention; the output pass with
+its operands in LDS or read from memory) at lengths that are not multiples of
+the tile sizes.  Bar as in the other parity tests: relative L2 1e-5 for fp32
+inputs, 2e-2 for bf16 inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.native as native
+import oracle.reference as ref
+import positive_random_feature_amd as favor
+from positive_random_feature_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+N_CASES = 40
+
+
+def _draw_cases(n, seed=20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = str(rng.choice(["bf16", "bf16", "f32"]))
+        d = int(rng.choice([16, 32, 64, 128] if dtype == "bf16" else [16, 32, 64]))
+        op = str(rng.choice(["bidir", "causal"]))
+        feature = str(rng.choice(["positive", "positive", "relu"]))
+        if op == "causal":
+            ms = [32, 64, 128, 256, 512]
+            if dtype == "f32" and d == 64:
+                ms = ms[:-1]
+        else:
+            ms = list(range(32, 257, 32)) + [320, 384, 448, 512]
+        m = int(rng.choice(ms))
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 4))
+        # the ReLU causal oracle walks the tokens in Python: shorter sequences
+        L = int(rng.integers(1, 400 if (feature == "relu" and op == "causal") else 1200))
+        per_head = bool(rng.integers(0, 2))
+        cases.append((i, dtype, d, m, op, feature, B, H, L, per_head))
+    return cases
+
+
+CASES = _draw_cases(N_CASES)
+
+
+def _id(c):
+    i, dtype, d, m, op, feature, B, H, L, per_head = c
+    return f"{i}-{op}-{feature}-{dtype}-d{d}-m{m}-{B}x{H}x{L}-{'perhead' if per_head else 'shared'}"
+
+
+def _to_dev(inp, dtype, dev):
+    if dtype == "bf16":
+        return [torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
+    return [torch.from_numpy(a).to(dev) for a in (inp.q, inp.k, inp.v)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_id(c) for c in CASES])
+def test_random_shape(case):
+    i, dtype, d, m, op, feature, B, H, L, per_head = case
+    print(f"[sweep] {_id(case)}", flush=True)
+    base = WORKLOADS["causal_bf16_8k" if dtype == "bf16" else "bidir_f32_tiny"]
+    w = base.replace(d=d, m=m, omega_per_head=per_head)
+    inp = make_inputs(w, B=B, H=H, L=L, seed=5000 + i)
+    om = ref.orf_omega(7000 + i, H if per_head else 1, m, d)
+    om = om if per_head else om[0]
+    dev = torch.device("cuda:0")
+    q, k, v = _to_dev(inp, dtype, dev)
+    fn = favor.bidir if op == "bidir" else favor.causal
+    got = fn(q, k, v, torch.from_numpy(om).to(dev), feature=feature)
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy().astype(np.float64)
+    if feature == "positive":
+        want = (native.bidir if op == "bidir" else native.causal)(inp.q, inp.k, inp.v, om)
+    else:
+        want = (ref.bidir if op == "bidir" else ref.causal)(inp.q, inp.k, inp.v, om, kind="relu")
+    assert np.isfinite(want).all()
+    err = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    print(f"[sweep] {_id(case)}: rel L2 {err:.3e} (tol {TOL[dtype]})", flush=True)
+    assert err <= TOL[dtype]
