@@ -281,6 +281,9 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
     float M = 0.0f;
 
     const T* src[2] = {k + xbase, v + xbase};
+    // lane part of the transpose-read addresses of the V tiles: each read is
+    // then the step's slot base plus this offset plus a constant
+    const int voff = kappa_lane_off(lane, [](int row, int col) { return row * RS + col; });
     // PD steps in flight in registers (global latency).  Every unrolled step
     // stores, loads and meets the barrier (loads past the last step re-read
     // it, from cache), so the load count is static.
@@ -379,12 +382,23 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
                 const bool more = it + 1 < nsteps;
                 if (more) lm = project(it + 1, pn);
                 const T* vt = tiles[it % 3][1];
+                // the lane offset passes through an empty asm statement, so
+                // the compiler cannot hoist (offset + constant) pairs out of
+                // the loop into separate registers: every read below is one
+                // address per step plus an immediate
+                int vo = voff;
+                asm volatile("" : "+v"(vo));
+                const T* vl = vt + vo;
 #pragma unroll
                 for (int ks2 = 0; ks2 < 2; ++ks2) {
                     const T* vk = vt + 32 * ks2 * RS;
 #pragma unroll
                     for (int nt = 0; nt < NT - 1; ++nt) {
-                        const vec8<T> vb = kappa_col<RS>(vk, 16 * nt, lane);
+                        vec8<T> vb;
+                        if constexpr (sizeof(T) == 2)
+                            vb = kappa_col_at<RS>(vl + 32 * ks2 * RS + 16 * nt);
+                        else
+                            vb = kappa_col<RS>(vk, 16 * nt, lane);
 #pragma unroll
                         for (int ft = 0; ft < NFT; ++ft) kv[ft][nt] = mma32(a[ks2][ft], vb, kv[ft][nt]);
                     }
