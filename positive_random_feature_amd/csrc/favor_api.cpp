@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kTargetWorkgroups = 256;  // one per compute unit of an MI355X
+using favor::kTargetWorkgroups;
 static_assert(kTargetWorkgroups <= favor::kMaxSeg, "segments per head bounded by the plan");
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -8,6 +8,8 @@ namespace favor {
 
 // LDS available to one workgroup on gfx950.
 constexpr size_t kMaxLds = 160 * 1024;
+// Workgroups that fill the chip once: one per compute unit of an MI355X.
+constexpr int kTargetWorkgroups = 256;
 // Most segments per head the launch plan makes (the merge/scan pass keeps
 // their shifts in LDS).
 constexpr int kMaxSeg = 256;

@@ -1930,28 +1930,43 @@ static hipError_t launch_all(const LaunchArgs& a) {
     stage_event(a, 2);
     if (a.op == OpKind::Bidir) {
         constexpr int NTT = 2;
-        // waves per workgroup: sixteen where the registers allow (bf16,
-        // d <= 64), so each staging of the operands serves 512 queries
-        constexpr int NW = (sizeof(T) == 2 && D <= 64) ? 16 : 8;
-        const int tok_per_wg = NW * 16 * NTT;
-        const int blocks = (a.L + tok_per_wg - 1) / tok_per_wg;
         const size_t om_b = sizeof(vec8<T>) * 64 * (size_t)(a.m / 16) * KSD;
         const size_t kv_b = sizeof(vec8<T>) * 64 * (size_t)(D / 16 + 1) * (a.m / 32);
         const vec8<T>* kvp = reinterpret_cast<const vec8<T>*>(a.ws_kvpack);
-        if (om_b + kv_b <= kMaxLds) {
-            auto kern = bidir_out_kernel<T, D, true, true, NW, RELU>;
-            (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(om_b + kv_b));
-            hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), om_b + kv_b, st, q, ompack, om_head_vecs, kvp,
-                               a.ws_mmax, out, a.H, a.L, a.m);
-        } else if (kv_b <= kMaxLds) {
-            auto kern = bidir_out_kernel<T, D, false, true, NW, RELU>;
-            (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kv_b);
-            hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), kv_b, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,
-                               out, a.H, a.L, a.m);
+        auto launch_out = [&](auto nw_c) {
+            constexpr int NW = decltype(nw_c)::value;
+            const int tok_per_wg = NW * 16 * NTT;
+            const int blocks = (a.L + tok_per_wg - 1) / tok_per_wg;
+            if (om_b + kv_b <= kMaxLds) {
+                auto kern = bidir_out_kernel<T, D, true, true, NW, RELU>;
+                (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(om_b + kv_b));
+                hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), om_b + kv_b, st, q, ompack, om_head_vecs, kvp,
+                                   a.ws_mmax, out, a.H, a.L, a.m);
+            } else if (kv_b <= kMaxLds) {
+                auto kern = bidir_out_kernel<T, D, false, true, NW, RELU>;
+                (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kv_b);
+                hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), kv_b, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,
+                                   out, a.H, a.L, a.m);
+            } else {
+                auto kern = bidir_out_kernel<T, D, false, false, NW, RELU>;
+                hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), 0, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,
+                                   out, a.H, a.L, a.m);
+            }
+        };
+        // waves per workgroup: sixteen where the registers allow (bf16,
+        // d <= 64), so each staging of the operands serves 512 queries; twelve
+        // (384 queries) when sixteen-wave workgroups would leave compute units
+        // idle and twelve-wave ones still fit in one round (1 x 8 x 12288:
+        // 256 workgroups instead of 192)
+        if constexpr (sizeof(T) == 2 && D <= 64) {
+            const long long wg16 = (long long)BH * ((a.L + 511) / 512);
+            const long long wg12 = (long long)BH * ((a.L + 383) / 384);
+            if (wg16 < kTargetWorkgroups && wg12 <= kTargetWorkgroups)
+                launch_out(IntC<12>{});
+            else
+                launch_out(IntC<16>{});
         } else {
-            auto kern = bidir_out_kernel<T, D, false, false, NW, RELU>;
-            hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), 0, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,
-                               out, a.H, a.L, a.m);
+            launch_out(IntC<8>{});
         }
         stage_event(a, 3);
         return hipGetLastError();
