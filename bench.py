@@ -16,15 +16,19 @@ reported under "configs" with its algorithmic work and roofline fraction.
 rocprofv3 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of this script
 (with ``--calib-copy --no-configs``) into profiles/traffic.json;
 ``python bench.py --summarise-trace TRACE_DIR`` prints per-stage launch
-times from a ``--kernel-trace`` run.  ``python bench.py --workload NAME``
+times from a ``--kernel-trace`` run; ``python bench.py --summarise-sq D1 D2 D3``
+prints per-wave SQ counters from three ``--pmc`` passes (the counter sets
+listed in ``SQ_PASSES``).  ``python bench.py --workload NAME``
 runs one workload alone (stage-timed calls), for profiling it.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
 import hashlib
+import glob
 import json
 import os
 import re
@@ -347,7 +351,6 @@ def time_streaming(hip, dev, stream, name="causal_bf16_8k", pieces=8, reps=50):
 # Profiler summaries (rocprofv3 CSV output of runs of this script)
 # ---------------------------------------------------------------------------
 def _read_csvs(root, suffix):
-    import csv
     import glob
     rows = []
     for path in sorted(glob.glob(os.path.join(root, "**", "*" + suffix), recursive=True)):
@@ -420,6 +423,46 @@ def summarise_counters(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+SQ_PASSES = (
+    ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+     "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY"),
+    ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_LDS_BANK_CONFLICT",
+     "SQ_INSTS_VALU_TRANS_F32", "SQ_WAIT_INST_LDS"),
+    ("SQ_WAVES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VMEM_WR", "SQ_ACTIVE_INST_SCA",
+     "SQ_INSTS_VMEM_RD", "SQ_INST_CYCLES_VMEM_RD", "SQ_ACTIVE_INST_MISC"),
+)
+SQ_KERNELS = ("kv_partial", "merge_scan", "bidir_out", "causal_tile", "causal_wide", "causal_chunk", "features")
+
+
+def summarise_sq(dirs):
+    """Per-wave SQ counters of each kernel from three rocprofv3 --pmc runs
+    (one per entry of SQ_PASSES, in that order): every counter summed over
+    the kernel's dispatches and divided by that pass's SQ_WAVES."""
+    tot = [{} for _ in dirs]
+    for p, d in enumerate(dirs):
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    k = next((k for k in SQ_KERNELS if k + "_kernel" in r["Kernel_Name"]), None)
+                    if k is None:
+                        continue
+                    c = tot[p].setdefault(k, {})
+                    c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    print("| kernel | VALU instr | MFMA instr | exp/rcp instr | LDS instr | SALU instr | VALU busy (x4 cyc) "
+          "| MFMA busy (cyc) | LDS wait (x4 cyc) | wave life (x4 cyc) | LDS bank conflicts (cyc) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for k in SQ_KERNELS:
+        if not all(k in t for t in tot):
+            continue
+        a, b, c = (t[k] for t in tot)
+        w1, w2, w3 = a["SQ_WAVES"], b["SQ_WAVES"], c["SQ_WAVES"]
+        vals = (b["SQ_INSTS_VALU"] / w2, b["SQ_INSTS_MFMA"] / w2, b["SQ_INSTS_VALU_TRANS_F32"] / w2,
+                b["SQ_INSTS_LDS"] / w2, b["SQ_INSTS_SALU"] / w2, a["SQ_ACTIVE_INST_VALU"] / w1,
+                c["SQ_VALU_MFMA_BUSY_CYCLES"] / w3, b["SQ_WAIT_INST_LDS"] / w2, a["SQ_WAVE_CYCLES"] / w1,
+                b["SQ_LDS_BANK_CONFLICT"] / w2)
+        print(f"| {k}_kernel | " + " | ".join(f"{v:.0f}" for v in vals) + " |")
+
+
 def summarise_trace(trace_dir):
     rows = _read_csvs(trace_dir, "kernel_trace.csv")
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
@@ -448,6 +491,7 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload timings")
     ap.add_argument("--summarise-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarise-trace", metavar="TRACE_DIR")
+    ap.add_argument("--summarise-sq", nargs=3, metavar=("PASS1_DIR", "PASS2_DIR", "PASS3_DIR"))
     ap.add_argument("--workload", choices=sorted(WORKLOADS), help="time one workload alone, stage by stage")
     args = ap.parse_args()
     if args.summarise_counters:
@@ -456,8 +500,11 @@ def main():
     if args.summarise_trace:
         summarise_trace(args.summarise_trace)
         return
+    if args.summarise_sq:
+        summarise_sq(args.summarise_sq)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this build.",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library runs on one GPU and has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
