@@ -97,7 +97,9 @@ size_t favor_workspace_bytes(int op, const favor_shape *shape, int chunk);
  * The projection uses omega rounded to the input dtype (bf16 inputs: bf16
  * omega * log2(e), fp32 accumulation).  ws/ws_bytes: device workspace of at
  * least favor_workspace_bytes(FAVOR_OP_FEATURES, shape, 0) bytes, 256-byte
- * aligned.  phi must not overlap x; log_scale must not overlap phi.
+ * aligned.  phi must not overlap x or omega; log_scale must not overlap
+ * phi, x or omega; ws must not overlap x, omega, phi or log_scale
+ * (FAVOR_ERR_INVALID_ARG).
  */
 favor_status favor_features(const favor_shape *shape, const void *x, const float *omega, float *phi,
                             float *log_scale, int stabilize, void *ws, size_t ws_bytes, void *stream);
@@ -109,7 +111,9 @@ favor_status favor_features(const favor_shape *shape, const void *x, const float
  * ws/ws_bytes: device workspace of at least
  * favor_workspace_bytes(FAVOR_OP_BIDIR, shape, 0) bytes, 256-byte aligned;
  * its contents need not be initialised and are garbage afterwards.
- * out must not overlap q, k, v or ws.
+ * out must not overlap q, k, v, omega or ws, and ws must not overlap q, k,
+ * v or omega (FAVOR_ERR_INVALID_ARG): the kernels write the workspace while
+ * later kernels of the same call still read the inputs.
  */
 favor_status favor_bidir(const favor_shape *shape, const void *q, const void *k, const void *v,
                          const float *omega, void *out, void *ws, size_t ws_bytes, void *stream);
@@ -120,14 +124,46 @@ favor_status favor_bidir(const favor_shape *shape, const void *q, const void *k,
  * attention):
  *     out_t = phi(q_t)^T G_t / phi(q_t)^T (sum_{s<=t} phi(k_s)),
  * with an inclusive mask (position t attends to keys 0..t).
- * chunk: tokens per step of the chunked scan.  0 selects the library's
- * length for the shape: 64 for bf16 with d = 64 and m <= 256, 32 otherwise;
- * a nonzero value must equal that length (else FAVOR_ERR_UNSUPPORTED).
+ * chunk: tokens per step of the chunked scan (any length gives the same
+ * result up to rounding).  Accepted: 0 (the shape's default), 32, and 64
+ * where the shape has a 64-token scan: bf16 with d = 64 and m in
+ * {64, 128, 256} default to 64 (tile scan) and also accept 32
+ * (feature-split scan); every other shape accepts 32, its default.  Other
+ * values: FAVOR_ERR_UNSUPPORTED.
  * Workspace as for favor_bidir with FAVOR_OP_CAUSAL.
  */
 favor_status favor_causal(const favor_shape *shape, const void *q, const void *k, const void *v,
                           const float *omega, void *out, int chunk, void *ws, size_t ws_bytes,
                           void *stream);
+
+/*
+ * Launch-plan overrides, for tuning and for testing that the result does not
+ * depend on how the sequence is split ("paperlayer.ai" summary, A.2: the
+ * prefix sums run in O(log L) parallel time, so any split of the scan into
+ * segments gives the same result up to rounding).
+ *   chunk:    causal chunk length as for favor_causal (0 = default);
+ *             ignored by bidirectional attention.
+ *   segments: token segments per head, 0 = automatic (sized so that one
+ *             pass fills 256 compute units), else 1..256.  Segments are whole
+ *             32- or 64-token steps, so fewer may be used than requested
+ *             (at most ceil(L / 32)).  Negative or > 256:
+ *             FAVOR_ERR_INVALID_ARG.
+ * A NULL plan means both defaults.  The workspace size depends on the plan:
+ * favor_workspace_bytes_plan returns it (0 for an invalid shape or plan).
+ * The other arguments are those of favor_bidir / favor_causal.
+ */
+typedef struct {
+    int chunk;
+    int segments;
+} favor_plan;
+
+size_t favor_workspace_bytes_plan(int op, const favor_shape *shape, const favor_plan *plan);
+favor_status favor_bidir_plan(const favor_shape *shape, const void *q, const void *k, const void *v,
+                              const float *omega, void *out, const favor_plan *plan, void *ws, size_t ws_bytes,
+                              void *stream);
+favor_status favor_causal_plan(const favor_shape *shape, const void *q, const void *k, const void *v,
+                               const float *omega, void *out, const favor_plan *plan, void *ws, size_t ws_bytes,
+                               void *stream);
 
 /*
  * Causal FAVOR+ continuing from a carried prefix state, and the state after
@@ -147,7 +183,8 @@ favor_status favor_causal(const favor_shape *shape, const void *q, const void *k
  * as NULL: its shift still takes part in the key stabiliser.
  * state_out: NULL = not written; otherwise it receives the state including
  * this call's keys, with one shift per head.  state_out must not overlap
- * state_in, q, k, v, out, omega or ws (FAVOR_ERR_INVALID_ARG).  Both must be
+ * state_in, q, k, v, out, omega or ws, and state_in must not overlap out or
+ * ws (FAVOR_ERR_INVALID_ARG).  Both must be
  * 4-byte aligned.  L = 0 writes nothing.  Positive features only
  * (FAVOR_FEATURE_RELU: FAVOR_ERR_UNSUPPORTED).  Other arguments as for
  * favor_causal.

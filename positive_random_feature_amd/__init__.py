@@ -33,18 +33,39 @@ def _omega_stride(omega: torch.Tensor, H: int, m: int, d: int) -> int:
     raise ValueError(f"omega must be [m, d], [1, m, d] or [H, m, d]; got {tuple(omega.shape)}")
 
 
-def _check_inputs(tensors, omega):
-    dev = tensors[0].device
-    if dev.type != "cuda":
-        raise ValueError("tensors must be on a GPU device")
-    dt = tensors[0].dtype
+def _check_inputs(tensors, omega, out=None, workspace=None):
+    """q, k, v (or x), omega and the optional out and workspace: shapes,
+    dtypes and layout first (host-side, before anything touches a device),
+    then that every tensor is on the inputs' GPU."""
+    x = tensors[0]
+    dt = x.dtype
     if dt not in _DTYPES:
         raise TypeError(f"unsupported dtype {dt}")
+    if x.dim() != 4:
+        raise ValueError(f"inputs must be [B, H, L, d]; got {tuple(x.shape)}")
     for t in tensors:
-        if t.device != dev or t.dtype != dt or t.dim() != 4 or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous [B, H, L, d] tensors of one dtype on one device")
-    if omega.device != dev or omega.dtype != torch.float32 or not omega.is_contiguous():
-        raise ValueError("omega must be a contiguous float32 tensor on the same device")
+        if tuple(t.shape) != tuple(x.shape):
+            raise ValueError(f"q, k, v must have one shape; got {tuple(x.shape)} and {tuple(t.shape)}")
+        if t.dtype != dt:
+            raise ValueError("q, k, v must have one dtype")
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    if omega.dtype != torch.float32 or not omega.is_contiguous():
+        raise ValueError("omega must be a contiguous float32 tensor")
+    if omega.dim() not in (2, 3):
+        raise ValueError(f"omega must be [m, d], [1, m, d] or [H, m, d]; got {tuple(omega.shape)}")
+    _omega_stride(omega, x.shape[1], omega.shape[-2], x.shape[3])
+    if out is not None and (tuple(out.shape) != tuple(x.shape) or out.dtype != dt or not out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous {dt} tensor of shape {tuple(x.shape)}")
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.dim() != 1
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    for t in list(tensors) + [omega] + [t for t in (out, workspace) if t is not None]:
+        if t.device != dev:
+            raise ValueError("q, k, v, omega, out and workspace must be on one device")
     return dev, dt
 
 
@@ -58,14 +79,21 @@ def _shape(x: torch.Tensor, omega: torch.Tensor, feature: str = "positive") -> _
     return _lib.shape(B, H, L, d, m, _DTYPES[x.dtype], _omega_stride(omega, H, m, d), _FEATURES[feature])
 
 
-def workspace_bytes(op: int, shp: _lib.FavorShape) -> int:
-    return int(_lib.load().favor_workspace_bytes(op, ctypes.byref(shp), 0))
+def workspace_bytes(op: int, shp: _lib.FavorShape, chunk: int = 0, segments: int = 0) -> int:
+    """Workspace bytes of one call (0: invalid shape or plan)."""
+    pl = _lib.plan(chunk, segments)
+    return int(_lib.load().favor_workspace_bytes_plan(op, ctypes.byref(shp), ctypes.byref(pl)))
 
 
-def _workspace(op: int, shp: _lib.FavorShape, dev) -> torch.Tensor:
-    n = workspace_bytes(op, shp)
+def _workspace(op: int, shp: _lib.FavorShape, dev, chunk: int = 0, segments: int = 0,
+               given: torch.Tensor | None = None) -> torch.Tensor:
+    n = workspace_bytes(op, shp, chunk, segments)
     if n == 0:
-        raise FavorError(2, "favor_workspace_bytes")
+        raise FavorError(2, "favor_workspace_bytes_plan")
+    if given is not None:
+        if given.numel() < n:
+            raise ValueError(f"workspace holds {given.numel()} bytes; this call needs {n}")
+        return given
     return torch.empty(n, dtype=torch.uint8, device=dev)
 
 
@@ -96,15 +124,17 @@ def features(x: torch.Tensor, omega: torch.Tensor, stabilize: bool = False, feat
 
 def bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, omega: torch.Tensor,
           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-          feature: str = "positive") -> torch.Tensor:
-    """Bidirectional FAVOR+: phi(Q)(phi(K)^T V) / phi(Q)(phi(K)^T 1)."""
-    dev, dt = _check_inputs([q, k, v], omega)
+          feature: str = "positive", segments: int = 0) -> torch.Tensor:
+    """Bidirectional FAVOR+: phi(Q)(phi(K)^T V) / phi(Q)(phi(K)^T 1).
+    ``segments``: token segments per head of the reduction (0 = automatic)."""
+    dev, dt = _check_inputs([q, k, v], omega, out, workspace)
     shp = _shape(q, omega, feature)
     out = torch.empty_like(q) if out is None else out
-    ws = _workspace(_lib.FAVOR_OP_BIDIR, shp, dev) if workspace is None else workspace
-    st = _lib.load().favor_bidir(ctypes.byref(shp), q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(),
-                                 out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
-    _lib.check(st, "favor_bidir")
+    ws = _workspace(_lib.FAVOR_OP_BIDIR, shp, dev, 0, segments, workspace)
+    pl = _lib.plan(0, segments)
+    st = _lib.load().favor_bidir_plan(ctypes.byref(shp), q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(),
+                                      out.data_ptr(), ctypes.byref(pl), ws.data_ptr(), ws.numel(), _stream(dev))
+    _lib.check(st, "favor_bidir_plan")
     return out
 
 
@@ -123,24 +153,32 @@ def state_parts(state: torch.Tensor, m: int, d: int):
 
 def causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, omega: torch.Tensor, chunk: int = 0,
            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-           state: torch.Tensor | None = None, return_state: bool = False, feature: str = "positive"):
+           state: torch.Tensor | None = None, return_state: bool = False, feature: str = "positive",
+           segments: int = 0):
     """Causal FAVOR+ through the prefix-sum state G_t = sum_{s<=t} phi(k_s) v_s^T.
 
+    ``chunk``: tokens per scan step (0 = the shape's default; 32, or 64 where
+    the shape has a 64-token scan).  ``segments``: token segments per head
+    (0 = automatic).
     ``state`` ([B, H, m (d + 1) + 1] float32 on the device, or None) carries
     the prefix of keys seen by earlier calls; with ``return_state`` the state
     including this call's keys is returned as well: (out, state).
     ``feature="relu"`` selects the generalised ReLU features (no carried state).
     """
-    dev, dt = _check_inputs([q, k, v], omega)
+    dev, dt = _check_inputs([q, k, v], omega, out, workspace)
     shp = _shape(q, omega, feature)
     out = torch.empty_like(q) if out is None else out
-    ws = _workspace(_lib.FAVOR_OP_CAUSAL, shp, dev) if workspace is None else workspace
     lib = _lib.load()
     if state is None and not return_state:
-        st = lib.favor_causal(ctypes.byref(shp), q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(),
-                              out.data_ptr(), int(chunk), ws.data_ptr(), ws.numel(), _stream(dev))
-        _lib.check(st, "favor_causal")
+        ws = _workspace(_lib.FAVOR_OP_CAUSAL, shp, dev, chunk, segments, workspace)
+        pl = _lib.plan(chunk, segments)
+        st = lib.favor_causal_plan(ctypes.byref(shp), q.data_ptr(), k.data_ptr(), v.data_ptr(), omega.data_ptr(),
+                                   out.data_ptr(), ctypes.byref(pl), ws.data_ptr(), ws.numel(), _stream(dev))
+        _lib.check(st, "favor_causal_plan")
         return out
+    if segments:
+        raise ValueError("segments cannot be chosen together with a carried state")
+    ws = _workspace(_lib.FAVOR_OP_CAUSAL, shp, dev, chunk, 0, workspace)
     B, H, _L, d = q.shape
     n = state_floats(shp.m, d)
     if state is not None:

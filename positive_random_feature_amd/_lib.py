@@ -33,6 +33,13 @@ class FavorShape(ctypes.Structure):
     ]
 
 
+class FavorPlan(ctypes.Structure):
+    _fields_ = [
+        ("chunk", ctypes.c_int),
+        ("segments", ctypes.c_int),
+    ]
+
+
 class FavorError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -59,6 +66,13 @@ def load() -> ctypes.CDLL:
     lib.favor_bidir.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.favor_causal.restype = ctypes.c_int
     lib.favor_causal.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    pp = ctypes.POINTER(FavorPlan)
+    lib.favor_workspace_bytes_plan.restype = sz
+    lib.favor_workspace_bytes_plan.argtypes = [ctypes.c_int, sp, pp]
+    lib.favor_bidir_plan.restype = ctypes.c_int
+    lib.favor_bidir_plan.argtypes = [sp, vp, vp, vp, vp, vp, pp, vp, sz, vp]
+    lib.favor_causal_plan.restype = ctypes.c_int
+    lib.favor_causal_plan.argtypes = [sp, vp, vp, vp, vp, vp, pp, vp, sz, vp]
     lib.favor_causal_state.restype = ctypes.c_int
     lib.favor_causal_state.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp]
     for name, chunk in (("favor_bidir_profiled", False), ("favor_causal_profiled", True)):
@@ -79,6 +93,10 @@ def load() -> ctypes.CDLL:
 def shape(B: int, H: int, L: int, d: int, m: int, dtype: int, omega_head_stride: int,
           feature: int = FAVOR_FEATURE_POSITIVE) -> FavorShape:
     return FavorShape(B, H, L, d, m, dtype, omega_head_stride, feature)
+
+
+def plan(chunk: int = 0, segments: int = 0) -> FavorPlan:
+    return FavorPlan(int(chunk), int(segments))
 
 
 def check(status: int, where: str) -> None:

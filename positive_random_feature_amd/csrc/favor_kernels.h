@@ -29,6 +29,7 @@ struct LaunchArgs {
     float* log_scale;
     int stabilize;
     int nseg, seg_len;  // segments per head and their length (multiple of 32)
+    int chunk;          // causal: tokens per scan step (32 or 64)
     // workspace regions
     void* ws_ompack;
     float* ws_partial;

@@ -95,7 +95,9 @@ extern "C" favor_status favor_hadamard_omega(unsigned long long seed, int n_head
                                              void* stream) {
     if (!omega || ((uintptr_t)omega % 16) != 0 || n_heads < 1 || m < 1) return FAVOR_ERR_INVALID_ARG;
     if (d != 16 && d != 32 && d != 64 && d != 128) return FAVOR_ERR_UNSUPPORTED;
-    if ((long long)n_heads * m * d >= (1LL << 31)) return FAVOR_ERR_UNSUPPORTED;
+    // n_heads * m * d < 2^31; n_heads * m < 2^62 cannot overflow, and the
+    // bound is checked before the last factor
+    if ((long long)n_heads * m >= (1LL << 31) / d) return FAVOR_ERR_UNSUPPORTED;
     const long long rows = (long long)n_heads * m;
     const dim3 grid((unsigned)((rows + 63) / 64));
     hipStream_t st = static_cast<hipStream_t>(stream);

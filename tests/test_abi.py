@@ -18,6 +18,7 @@ OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 # fake, 256-byte-aligned device addresses: validation rejects the call before
 # any of them is touched
 P_Q, P_K, P_V, P_O, P_OM, P_WS = (0x10000000 * (i + 1) for i in range(6))
+P_S1, P_S2 = 0x70000000, 0x78000000  # fake state buffers, far from the others
 
 
 @pytest.fixture(scope="module")
@@ -85,6 +86,10 @@ def test_validation(lib, fn):
     assert fn(lib, shp(), q=P_Q + 8) == INVALID          # 16-byte alignment
     assert fn(lib, shp(), o=P_Q) == INVALID              # out aliases q
     assert fn(lib, shp(), o=P_V + 64) == INVALID         # out overlaps v
+    assert fn(lib, shp(), o=P_OM) == INVALID             # out overlaps omega
+    for p in (P_Q, P_K, P_V, P_OM):                     # the workspace overlaps an input
+        assert fn(lib, shp(), ws=p) == INVALID
+    assert fn(lib, shp(), ws=P_K - 256) == INVALID       # ... partly
     assert fn(lib, shp(), ws=None) == WORKSPACE
     assert fn(lib, shp(), ws=P_WS + 16) == WORKSPACE     # 256-byte alignment
     need = lib.favor_workspace_bytes(1 if fn is _bidir else 2, ctypes.byref(shp()), 0)
@@ -118,9 +123,16 @@ def test_support_matrix_matches_header(lib):
 def test_causal_chunk_and_lds_limits(lib):
     # A one-byte workspace makes an accepted shape stop at the workspace
     # check (WORKSPACE), before anything is launched.
-    # chunk: 0 or the library's length for the shape (64: bf16, d=64, m<=256; else 32)
-    assert _causal(lib, shp(), chunk=64, nbytes=1) == WORKSPACE
-    assert _causal(lib, shp(), chunk=32, nbytes=1) == UNSUPPORTED
+    # chunk: 0, 32, and 64 where the shape has the 64-token tile scan
+    # (bf16, d=64, m in {64, 128, 256})
+    for m in (64, 128, 256):
+        assert _causal(lib, shp(m=m), chunk=64, nbytes=1) == WORKSPACE
+        assert _causal(lib, shp(m=m), chunk=32, nbytes=1) == WORKSPACE
+    for chunk in (16, 48, 128, 96):
+        assert _causal(lib, shp(), chunk=chunk, nbytes=1) == UNSUPPORTED
+    assert _causal(lib, shp(m=32), chunk=64, nbytes=1) == UNSUPPORTED
+    assert _causal(lib, shp(d=128, m=512), chunk=64, nbytes=1) == UNSUPPORTED
+    assert _causal(lib, shp(dtype=_lib.FAVOR_F32), chunk=64, nbytes=1) == UNSUPPORTED
     assert _causal(lib, shp(d=32, m=64), chunk=32, nbytes=1) == WORKSPACE
     assert _causal(lib, shp(d=32, m=64), chunk=64, nbytes=1) == UNSUPPORTED
     assert _causal(lib, shp(m=512), chunk=32, nbytes=1) == WORKSPACE
@@ -139,6 +151,11 @@ def test_features_validation(lib):
     assert f(ctypes.byref(s), P_Q, P_OM, P_O, None, 1, P_WS, 1 << 40, None) == INVALID   # log_scale needed
     assert f(ctypes.byref(s), P_Q, P_OM, P_Q, None, 0, P_WS, 1 << 40, None) == INVALID   # phi overlaps x
     assert f(ctypes.byref(s), P_Q, P_OM, P_O, None, 0, P_WS, 16, None) == WORKSPACE
+    assert f(ctypes.byref(s), P_Q, P_OM, P_OM, None, 0, P_WS, 1 << 40, None) == INVALID  # phi overlaps omega
+    assert f(ctypes.byref(s), P_Q, P_OM, P_O, P_Q, 1, P_WS, 1 << 40, None) == INVALID   # log_scale overlaps x
+    for ws in (P_Q, P_OM, P_O):                                                          # ws overlaps x, omega, phi
+        assert f(ctypes.byref(s), P_Q, P_OM, P_O, None, 0, ws, 1 << 40, None) == INVALID
+    assert f(ctypes.byref(s), P_Q, P_OM, P_O, P_S1, 1, P_S1, 1 << 40, None) == INVALID  # ... or log_scale
 
 
 @pytest.mark.parametrize("seed,H,m,d", [(0, 1, 32, 16), (0, 8, 256, 64), (3, 2, 40, 16), (11, 1, 512, 128), (5, 3, 10, 4)])
@@ -158,7 +175,6 @@ def test_orf_omega_invalid(lib):
     assert lib.favor_orf_omega(0, 1, -4, 4, out.ctypes.data) == INVALID
 
 
-P_S1, P_S2 = 0x70000000, 0x78000000  # fake state buffers, far from the others
 
 
 def _causal_state(lib, s, si=P_S1, so=P_S2, chunk=0, o=P_O, ws=P_WS, nbytes=1 << 40):
@@ -177,7 +193,9 @@ def test_causal_state_validation(lib):
     assert _causal_state(lib, shp(), si=P_WS + 1024, so=None) == INVALID  # state_in inside the workspace
     assert _causal_state(lib, shp(), si=P_S1 + 2) == INVALID         # 4-byte alignment
     assert _causal_state(lib, shp(), so=P_S2 + 2) == INVALID
-    assert _causal_state(lib, shp(), chunk=32) == UNSUPPORTED        # chunk as for favor_causal
+    assert _causal_state(lib, shp(), chunk=16) == UNSUPPORTED        # chunk as for favor_causal
+    assert _causal_state(lib, shp(d=32, m=64), chunk=64) == UNSUPPORTED
+    assert _causal_state(lib, shp(), si=P_O, so=None) == INVALID     # state_in overlaps out
     assert _causal_state(lib, shp(), nbytes=1) == WORKSPACE
     assert _causal_state(lib, shp(L=0), o=None, ws=None, nbytes=0) == OK  # L = 0: no-op, nothing written
 
@@ -200,3 +218,40 @@ def test_hadamard_omega_validation(lib):
     assert f(0, 1, 0, 16, P_OM, None) == INVALID
     assert f(0, 1, 32, 48, P_OM, None) == UNSUPPORTED   # d must be 16, 32, 64 or 128
     assert f(0, 1 << 12, 1 << 12, 128, P_OM, None) == UNSUPPORTED  # >= 2^31 elements
+
+
+def _causal_plan(lib, s, chunk=0, segments=0, ws=P_WS, nbytes=1 << 40):
+    pl = _lib.plan(chunk, segments)
+    return lib.favor_causal_plan(ctypes.byref(s), P_Q, P_K, P_V, P_OM, P_O, ctypes.byref(pl), ws, nbytes, None)
+
+
+def _bidir_plan(lib, s, segments=0, ws=P_WS, nbytes=1 << 40, plan=True):
+    pl = _lib.plan(0, segments)
+    return lib.favor_bidir_plan(ctypes.byref(s), P_Q, P_K, P_V, P_OM, P_O, ctypes.byref(pl) if plan else None, ws,
+                                nbytes, None)
+
+
+def test_plan_validation(lib):
+    """Plan overrides: segments in [0, 256], chunk as for favor_causal; the
+    workspace follows the plan."""
+    s = shp(B=2, H=8, L=8192)
+    for fn in (_causal_plan, _bidir_plan):
+        assert fn(lib, s, segments=-1) == INVALID
+        assert fn(lib, s, segments=257) == INVALID
+        assert fn(lib, s, segments=1, nbytes=1) == WORKSPACE
+        assert fn(lib, s, segments=256, nbytes=1) == WORKSPACE
+    assert _bidir_plan(lib, s, plan=False, nbytes=1) == WORKSPACE   # NULL plan: defaults
+    assert _causal_plan(lib, s, chunk=16, nbytes=1) == UNSUPPORTED
+    assert _causal_plan(lib, s, chunk=32, nbytes=1) == WORKSPACE
+    sz = lambda op, chunk=0, seg=0: lib.favor_workspace_bytes_plan(op, ctypes.byref(s), ctypes.byref(_lib.plan(chunk, seg)))
+    # the default plan is the plain entry points' plan
+    assert sz(2) == lib.favor_workspace_bytes(2, ctypes.byref(s), 0)
+    assert sz(1) == lib.favor_workspace_bytes(1, ctypes.byref(s), 0)
+    assert lib.favor_workspace_bytes_plan(2, ctypes.byref(s), None) == sz(2)
+    # fewer segments, less workspace; invalid plans report 0
+    assert 0 < sz(2, seg=1) < sz(2, seg=4) < sz(2, seg=64)
+    assert sz(1, seg=1) < sz(1)
+    assert sz(2, chunk=16) == 0 and sz(2, seg=-3) == 0 and sz(2, seg=300) == 0
+    # the workspace of the requested plan is what the call checks
+    need = sz(2, seg=3)
+    assert _causal_plan(lib, s, segments=3, nbytes=need - 1) == WORKSPACE
