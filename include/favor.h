@@ -194,6 +194,30 @@ favor_status favor_causal_state(const favor_shape *shape, const void *q, const v
                                 float *state_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Causal FAVOR+ that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * favor_causal, without ws/ws_bytes: the workspace is a static device array
+ * of FAVOR_NOALLOC_SCRATCH_BYTES (96 MiB) inside the library, one per GPU,
+ * held from the first call on that GPU until the process ends.
+ *   - A shape whose workspace (favor_workspace_bytes(FAVOR_OP_CAUSAL, shape,
+ *     chunk)) exceeds FAVOR_NOALLOC_SCRATCH_BYTES returns
+ *     FAVOR_ERR_WORKSPACE before any launch; invalid arguments are reported
+ *     as by favor_causal.
+ *   - The array belongs to the current device (hipGetDevice); `stream` must
+ *     belong to it too.  The first call on a device resolves the array's
+ *     address (hipGetSymbolAddress); make that call outside graph capture.
+ *   - Every call on one GPU shares its array: calls that overlap in time on
+ *     one GPU (different streams, or different host threads without
+ *     ordering) race and give wrong results.  Calls ordered on one stream
+ *     are safe; nothing in the array needs clearing between calls.
+ *   - No hipMalloc, hipFree or other allocation happens in the call.
+ */
+#define FAVOR_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+favor_status favor_causal_noalloc(const favor_shape *shape, const void *q, const void *k, const void *v,
+                                  const float *omega, void *out, int chunk, void *stream);
+
+/*
  * Stage-timed variants.  Identical results to favor_bidir / favor_causal;
  * additionally, events[i] (caller-created hipEvent_t handles) is recorded on
  * `stream` before stage i and events[FAVOR_N_STAGES] after the last stage.

@@ -14,7 +14,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["features", "bidir", "causal", "orf_omega", "hadamard_omega", "workspace_bytes", "state_floats",
+__all__ = ["features", "bidir", "causal", "causal_noalloc", "orf_omega", "hadamard_omega", "workspace_bytes", "state_floats",
            "state_parts", "FavorError"]
 
 FavorError = _lib.FavorError
@@ -192,6 +192,20 @@ def causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, omega: torch.Tenso
                                 _stream(dev))
     _lib.check(st, "favor_causal_state")
     return (out, new_state) if return_state else out
+
+
+def causal_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, omega: torch.Tensor, out: torch.Tensor,
+                   chunk: int = 0) -> torch.Tensor:
+    """Causal FAVOR+ through favor_causal_noalloc: no workspace argument and
+    no allocation in the call (the library's static per-GPU scratch array of
+    FAVOR_NOALLOC_SCRATCH_BYTES is used); ``out`` must be provided.  Calls
+    that overlap in time on one GPU race on that array."""
+    dev, dt = _check_inputs([q, k, v], omega, out)
+    shp = _shape(q, omega)
+    st = _lib.load().favor_causal_noalloc(ctypes.byref(shp), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          omega.data_ptr(), out.data_ptr(), int(chunk), _stream(dev))
+    _lib.check(st, "favor_causal_noalloc")
+    return out
 
 
 def orf_omega(seed: int, n_heads: int, m: int, d: int) -> torch.Tensor:

@@ -15,6 +15,7 @@ FAVOR_OP_CAUSAL = 2
 FAVOR_N_STAGES = 3
 FAVOR_FEATURE_POSITIVE = 0
 FAVOR_FEATURE_RELU = 1
+FAVOR_NOALLOC_SCRATCH_BYTES = 96 << 20
 
 STATUS = {0: "FAVOR_OK", 1: "FAVOR_ERR_INVALID_ARG", 2: "FAVOR_ERR_UNSUPPORTED", 3: "FAVOR_ERR_WORKSPACE",
           4: "FAVOR_ERR_HIP"}
@@ -73,6 +74,8 @@ def load() -> ctypes.CDLL:
     lib.favor_bidir_plan.argtypes = [sp, vp, vp, vp, vp, vp, pp, vp, sz, vp]
     lib.favor_causal_plan.restype = ctypes.c_int
     lib.favor_causal_plan.argtypes = [sp, vp, vp, vp, vp, vp, pp, vp, sz, vp]
+    lib.favor_causal_noalloc.restype = ctypes.c_int
+    lib.favor_causal_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     lib.favor_causal_state.restype = ctypes.c_int
     lib.favor_causal_state.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, sz, vp]
     for name, chunk in (("favor_bidir_profiled", False), ("favor_causal_profiled", True)):

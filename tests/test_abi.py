@@ -255,3 +255,20 @@ def test_plan_validation(lib):
     # the workspace of the requested plan is what the call checks
     need = sz(2, seg=3)
     assert _causal_plan(lib, s, segments=3, nbytes=need - 1) == WORKSPACE
+
+
+def test_noalloc_validation(lib):
+    """The entry point without a workspace validates like favor_causal and
+    refuses shapes whose workspace exceeds its static scratch array, all
+    before any HIP call."""
+    f = lib.favor_causal_noalloc
+    assert f(None, P_Q, P_K, P_V, P_OM, P_O, 0, None) == INVALID
+    assert f(ctypes.byref(shp(B=0)), P_Q, P_K, P_V, P_OM, P_O, 0, None) == INVALID
+    assert f(ctypes.byref(shp(d=48)), P_Q, P_K, P_V, P_OM, P_O, 0, None) == UNSUPPORTED
+    assert f(ctypes.byref(shp()), P_Q, P_K, P_V, P_OM, P_O, 16, None) == UNSUPPORTED
+    big = shp(B=1, H=256, L=128, d=128, m=512)
+    assert lib.favor_workspace_bytes(2, ctypes.byref(big), 0) > _lib.FAVOR_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), P_Q, P_K, P_V, P_OM, P_O, 0, None) == WORKSPACE
+    # the benchmarked causal workloads fit
+    for s in (shp(B=2, H=8, L=8192), shp(B=1, H=16, L=65536, d=128, m=512)):
+        assert 0 < lib.favor_workspace_bytes(2, ctypes.byref(s), 0) <= _lib.FAVOR_NOALLOC_SCRATCH_BYTES
