@@ -276,13 +276,69 @@ def features_relu(x: np.ndarray, omega: np.ndarray) -> np.ndarray:
     return np.maximum(proj, 0.0) / np.sqrt(m)
 
 
+def features_trig(x: np.ndarray, omega: np.ndarray) -> np.ndarray:
+    """Trigonometric random features of the softmax kernel, the estimator the
+    pages compare positive features against ([P1] Digest: the cos/sin
+    features of Rahimi and Recht; [P3] section 3, empirical approximation):
+
+        phi(x) = m**-1/2 * exp(|x|^2 / 2) * [sin(omega_i . x), cos(omega_i . x)]_i
+
+    so phi(x) . phi(y) = exp((|x|^2 + |y|^2)/2) * (1/m) sum_i cos(omega_i . (x - y)),
+    whose expectation over omega ~ N(0, I_d) is exp(x . y) (the Gaussian
+    characteristic function gives E cos(omega . z) = exp(-|z|^2 / 2)).
+    ``x`` is [..., d], ``omega`` [m, d]; returns [..., 2m] in float64 (sines
+    first).  Its values can be negative, so normalisers built from it can
+    change sign.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    omega = np.asarray(omega, dtype=np.float64)
+    m = omega.shape[-2]
+    proj = x @ omega.T
+    scale = np.exp(0.5 * np.sum(x * x, axis=-1, keepdims=True)) / np.sqrt(m)
+    return scale * np.concatenate([np.sin(proj), np.cos(proj)], axis=-1)
+
+
+def sm_hat_trig(x: np.ndarray, y: np.ndarray, omega: np.ndarray) -> np.ndarray:
+    """Trigonometric estimate of exp(x . y): phi_trig(x) . phi_trig(y), for
+    ``omega`` [m, d] or many independent draws [R, m, d] (returns [R])."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    omega = np.asarray(omega, dtype=np.float64)
+    m = omega.shape[-2]
+    z = x - y
+    return np.exp(0.5 * (np.dot(x, x) + np.dot(y, y))) * np.sum(np.cos(omega @ z), axis=-1) / m
+
+
+def trig_mse(x: np.ndarray, y: np.ndarray, m: int) -> float:
+    """MSE of the trigonometric estimator with m i.i.d. Gaussian rows:
+    exp(|x|^2 + |y|^2) * (1 - exp(-|x - y|^2))^2 / (2m), from
+    Var cos(omega . z) = E cos^2 - (E cos)^2 = (1 + e^{-2|z|^2})/2 - e^{-|z|^2}.
+    (The pages state only that this error explodes where the softmax kernel
+    is small, [P1] Theoretical bounds; the closed form is the mathematics of
+    the estimator.)"""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    z2 = float(np.sum((x - y) ** 2))
+    return float(np.exp(np.dot(x, x) + np.dot(y, y)) * (1.0 - np.exp(-z2)) ** 2 / (2.0 * m))
+
+
+def iid_omega(seed: int, m: int, d: int) -> np.ndarray:
+    """m i.i.d. N(0, I_d) projection rows (float32, numpy PCG64 seeded
+    [seed, 7]): the unstructured projection the orthogonal one is compared
+    with ([P1] Theoretical bounds, Theorem 2)."""
+    rng = np.random.default_rng([seed, 7])
+    return rng.standard_normal((m, d)).astype(np.float32)
+
+
 def feature_map(kind: str):
-    """The feature map of a kind: "positive" (softmax kernel, the default) or
-    "relu"."""
+    """The feature map of a kind: "positive" (softmax kernel, the default),
+    "relu", or "trig" (trigonometric features, 2m columns)."""
     if kind == "positive":
         return features
     if kind == "relu":
         return features_relu
+    if kind == "trig":
+        return features_trig
     raise ValueError(f"unknown feature kind {kind!r}")
 
 

@@ -527,3 +527,66 @@ def test_hadamard_signs_balanced_and_seeded():
     frac = (s > 0).mean()
     assert abs(frac - 0.5) <= 5 * 0.5 / np.sqrt(n)
     assert not np.array_equal(ref.hadamard_omega(1, 1, 32, 16), ref.hadamard_omega(2, 1, 32, 16))
+
+
+# ---------------------------------------------------------------------------
+# trigonometric features (the estimator the approximation study compares with)
+# ---------------------------------------------------------------------------
+
+def test_trig_features_self_identity():
+    """phi_trig(x) . phi_trig(x) = exp(|x|^2) for ANY projection (sin^2 + cos^2
+    = 1): pins the exp(|x|^2 / 2) scale and the m^-1/2 factor."""
+    rng = _rng(31)
+    for m, d in ((1, 3), (7, 16), (64, 16)):
+        om = rng.standard_normal((m, d)) * 3.0
+        x = rng.standard_normal(d) * 0.7
+        phi = ref.features_trig(x, om)
+        assert phi.shape == (2 * m,)
+        np.testing.assert_allclose(phi @ phi, np.exp(x @ x), rtol=1e-13)
+        np.testing.assert_allclose(ref.sm_hat_trig(x, x, om), np.exp(x @ x), rtol=1e-13)
+        y = rng.standard_normal(d) * 0.7
+        np.testing.assert_allclose(ref.features_trig(x, om) @ ref.features_trig(y, om), ref.sm_hat_trig(x, y, om),
+                                   rtol=1e-12)
+
+
+@pytest.mark.parametrize("z2", [0.3, 1.0, 2.5])
+def test_trig_estimator_unbiased_with_closed_form_mse(z2):
+    """E[phi_trig(x).phi_trig(y)] = exp(x.y) over i.i.d. Gaussian rows (within
+    5 standard errors), and its empirical MSE matches
+    exp(|x|^2+|y|^2)(1-exp(-|x-y|^2))^2/(2m) within 5 standard errors.  A
+    sign slip (x + y in the cosine) or a lost scale fails one of them."""
+    rng = _rng(int(z2 * 100))
+    d, m, R = 16, 8, 200_000
+    x = rng.standard_normal(d)
+    x *= 0.5 / np.linalg.norm(x)
+    u = rng.standard_normal(d)
+    u *= math.sqrt(z2) / np.linalg.norm(u)
+    y = x - u  # |x - y|^2 = z2
+    est = np.empty(R)
+    for c in range(0, R, 20000):
+        om = rng.standard_normal((20000, m, d))
+        est[c:c + 20000] = ref.sm_hat_trig(x, y, om)
+    target = math.exp(float(x @ y))
+    mse_cf = ref.trig_mse(x, y, m)
+    assert abs(est.mean() - target) <= 5 * math.sqrt(mse_cf / R)
+    sq = (est - target) ** 2
+    assert abs(sq.mean() - mse_cf) <= 5 * sq.std() / math.sqrt(R)
+
+
+def test_trig_attention_is_brute_force_of_its_features():
+    """Attention through trigonometric features by associativity equals the
+    explicit L x L form with the same features (normalisers can change sign,
+    so only the algebra is pinned here)."""
+    q, k, v = _qkv(41, 30, 4, scale=0.3)
+    om = _rng(42).standard_normal((12, 4))
+    want = ref.brute_force(q, k, v, om, causal_mask=False, kind="trig")
+    got = ref.bidir(q[None, None], k[None, None], v[None, None], om, kind="trig")[0, 0]
+    np.testing.assert_allclose(got, want, rtol=1e-9)
+
+
+def test_iid_omega_is_standard_normal():
+    om = ref.iid_omega(3, 4096, 16).astype(np.float64)
+    assert om.shape == (4096, 16)
+    assert abs(om.mean()) < 5 / math.sqrt(om.size)
+    assert abs(om.var() - 1.0) < 5 * math.sqrt(2.0 / om.size)
+    assert not np.array_equal(ref.iid_omega(3, 8, 16), ref.iid_omega(4, 8, 16))
