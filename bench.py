@@ -192,26 +192,73 @@ def traffic_for(stage: str):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(ops, min_seconds: float = 10.0, max_rounds: int = 50):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _rel_l2(got, want) -> float:
+    return float(np.linalg.norm(got - want) / np.linalg.norm(want))
+
+
+def cpu_baseline(ops, dev, stream, min_seconds: float = 10.0, max_rounds: int = 50):
     """The plain-C fp64 oracle on the host cores, over whole steps' inputs,
-    repeated until at least ``min_seconds`` of CPU work have been timed."""
+    repeated until at least ``min_seconds`` of CPU work have been timed.  The
+    oracle outputs it computes also give each workload's parity (rel L2 of
+    the library's output against the oracle on the same inputs): the two step
+    workloads and the other configurations over the whole output, the long
+    causal one on sampled rows of four heads (its full-tensor check runs in
+    the test suite)."""
     from oracle import native
+    from oracle import reference as ref
     native.build(force=False)
     t_total = 0.0
     tokens = 0
     rounds = 0
+    last = {}
     while rounds < max_rounds and (rounds == 0 or t_total < min_seconds):
         for op in ops:
             inp = op.inp
             fn = native.bidir if op.w.op == "bidir" else native.causal
             t0 = time.perf_counter()
-            fn(inp.q, inp.k, inp.v, op.omega_host)
+            last[op.w.name] = fn(inp.q, inp.k, inp.v, op.omega_host)
             t_total += time.perf_counter() - t0
             tokens += op.w.tokens
         rounds += 1
+    parity = {}
+    for op in ops:
+        op.run(stream)
+        torch.cuda.synchronize()
+        parity[op.w.name] = _rel_l2(op.out.float().cpu().numpy().astype(np.float64), last[op.w.name])
+    for name in ("bidir_f32_tiny", "bidir_bf16_12k", "causal_bf16_64k"):
+        op = Op(name, dev)
+        op.run(stream)
+        torch.cuda.synchronize()
+        got = op.out.float().cpu().numpy().astype(np.float64)
+        inp, w = op.inp, op.w
+        if name == "causal_bf16_64k":
+            rows = np.unique(np.concatenate([np.arange(0, w.L, 8192), np.arange(8191, w.L, 8192),
+                                             np.random.default_rng(3).integers(0, w.L, 24)]))
+            errs = []
+            for h in (0, 5, 10, 15):
+                want = ref.causal_rows(inp.q[0, h], inp.k[0, h], inp.v[0, h], op.omega_host[h], rows)
+                errs.append(_rel_l2(got[0, h, rows], want))
+            parity[name + " (sampled rows, 4 heads)"] = max(errs)
+        else:
+            fn = native.bidir if w.op == "bidir" else native.causal
+            parity[name] = _rel_l2(got, fn(inp.q, inp.k, inp.v, op.omega_host))
+        del op
     return {"value": tokens / t_total, "unit": "tokens/s", "cores": native.num_threads(), "kind": "oracle",
             "sample": f"{rounds} full steps (bidir 4x8x4096 + causal 2x8x8192, d=64, m=256) back to back, "
-                      "fp64 plain-C oracle, OpenMP over heads", "seconds": t_total}
+                      "fp64 plain-C oracle, OpenMP over heads", "seconds": t_total,
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "parity_rel_l2": parity}
 
 
 def alg_work(w):
@@ -232,10 +279,16 @@ def time_configs(hip, dev, stream, reps_target_ms: float = 20.0):
     step workloads also with the generalised ReLU features ("<name>:relu",
     the same algorithmic work without the exponentials)."""
     res = {}
-    runs = [(name, "positive") for name in WORKLOADS] + [("bidir_bf16_4k", "relu"), ("causal_bf16_8k", "relu")]
+    runs = [(name, "positive") for name in WORKLOADS] + [("bidir_bf16_4k", "relu"), ("causal_bf16_8k", "relu"),
+                                                         ("causal_bf16_8k", "chunk32")]
     for name, feature in runs:
         w = WORKLOADS[name]
-        op = Op(name, dev, feature)
+        if feature == "chunk32":  # the causal chunk length as a tunable: 32-token scan
+            w = w.replace(chunk=32)
+            op = Op(name, dev)
+            op.w = w
+        else:
+            op = Op(name, dev, feature)
         for _ in range(3):
             op.run(stream)
         torch.cuda.synchronize()
@@ -257,6 +310,8 @@ def time_configs(hip, dev, stream, reps_target_ms: float = 20.0):
         t_roof = max(t_mfma, t_hbm)
         res[name if feature == "positive" else f"{name}:{feature}"] = {
                      "op": w.op, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "m": w.m, "dtype": w.dtype,
+                     "chunk": (w.chunk or (64 if w.d == 64 and w.dtype == "bf16" and w.m <= 256 else 32))
+                     if w.op == "causal" else None,
                      "calls": n, "us_per_call": ms * 1e3, "tokens_per_s": w.tokens / (ms * 1e-3),
                      "alg_gflop": flops / 1e9, "alg_mb": bytes_ / 1e6, "bound": bound,
                      "roof_us": t_roof * 1e6, "frac": t_roof / (ms * 1e-3),
@@ -545,6 +600,18 @@ def main():
     ms_total = hip.elapsed_ms(e0, e1)
     ms_per_step = ms_total / args.steps
 
+    # each op alone, back to back without events between kernels (for the
+    # whole-op roofline fraction)
+    op_ms_plain = {}
+    for op in ops:
+        for _ in range(3):
+            op.run(stream)
+        hip.record(e0, stream)
+        for _ in range(args.steps):
+            op.run(stream)
+        hip.record(e1, stream)
+        op_ms_plain[op.w.name] = hip.elapsed_ms(e0, e1) / args.steps
+
     # stage-timed region: the same K steps with events between kernels
     n_ev = _lib.FAVOR_N_STAGES + 1
     evs = [[[hip.event() for _ in range(n_ev)] for _ in ops] for _ in range(args.steps)]
@@ -597,7 +664,11 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic_for(dom), "kernel_hash": traffic_kernel_hash(kname),
                      "alg_bytes_per_launch": alg_bytes,
-                     "avg_launch_ms": stage_ms[dom]},
+                     "avg_launch_ms": stage_ms[dom],
+                     # the whole operation of that kernel (all its kernels): its
+                     # algorithmic bytes over the step's per-op time
+                     "op_frac": alg_work(dom_op.w)[1] / (op_ms_plain[dom_op.w.name] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "op_us_per_call": op_ms_plain[dom_op.w.name] * 1e3},
         "per_op_tokens_per_s": {name: WORKLOADS[name].tokens / (ms * 1e-3) for name, ms in op_ms.items()},
         "stage_ms": stage_ms,
         "wall_s_timed_region": wall,
@@ -608,7 +679,7 @@ def main():
         result["streaming"] = time_streaming(hip, dev, stream)
         result["hadamard_projection"] = time_hadamard(hip, dev, stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(ops)
+        result["cpu_baseline"] = cpu_baseline(ops, dev, stream)
     print(json.dumps(result), flush=True)
 
 

@@ -57,7 +57,9 @@ struct CausalCfg {
 hipError_t launch(const LaunchArgs& a);
 // Tokens per step of the causal chunked scan for a shape.
 int causal_chunk_tokens(int dtype_bytes, int D, int m);
-CausalCfg causal_config(int D, int m);
+CausalCfg causal_config(int dtype_bytes, int D, int m);
+// Shapes whose causal scan is the d = 128 column-half scan (causal_wide).
+bool causal_wide_shape(int dtype_bytes, int D, int m);
 // LDS bytes the causal kernel needs (SIZE_MAX when the shape is unsupported).
 size_t causal_smem_bytes(int dtype_bytes, int D, int m);
 

@@ -106,6 +106,16 @@ __device__ __forceinline__ bf16x8 kappa_col_at(const bf16* p) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// The (up to three) tensors a prefetch moves, passed by value: element i is a
+// select between registers.  An array of pointers would be indexed at run
+// time (the compiler turns a select between two array loads into one load at
+// a selected index) and kept in scratch memory.
+template <typename P>
+struct Ptrs {
+    P p0, p1, p2;
+    __device__ __forceinline__ P at(int i) const { return i == 2 ? p2 : (i == 1 ? p1 : p0); }
+};
+
 // ---------------------------------------------------------------------------
 // Tile prefetch by NTHR threads (thread index taken modulo NTHR, so the
 // group can be any aligned block of NTHR threads): NTEN tensors, each a
@@ -140,27 +150,29 @@ struct Prefetch {
             cc = c % CH;
         }
     }
-    __device__ __forceinline__ void load(const T* const* src, int t0, int t_max) {
+    __device__ __forceinline__ void load(Ptrs<const T*> src, int t0, int t_max) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             int tn, cc;
             where(i, tn, cc);
             const int t = min(t0 + cc / CPR, t_max);
-            v[i] = gload8(src[tn] + (size_t)t * D + 8 * (cc % CPR));
+            v[i] = gload8(src.at(tn) + (size_t)t * D + 8 * (cc % CPR));
         }
     }
     // SWZ: the destination tiles use swz_tile (bf16, D = 64).  Tiles with
     // every row valid (the common case, a wave-uniform test) take a copy of
     // the code without the zeroing selects.
-    template <bool SWZ = false>
-    __device__ __forceinline__ void store(T* const* dst, float* nrm, int norm_mask, int t0, int t_end) const {
+    // NEG_TAIL: rows at or past t_end get the row constant -inf instead of
+    // that of a zero row, so a projection initialised with it masks them.
+    template <bool SWZ = false, bool NEG_TAIL = false>
+    __device__ __forceinline__ void store(Ptrs<T*> dst, float* nrm, int norm_mask, int t0, int t_end) const {
         if (t0 + ROWS <= t_end)
-            store_rows<SWZ, false>(dst, nrm, norm_mask, t0, t_end);
+            store_rows<SWZ, false, NEG_TAIL>(dst, nrm, norm_mask, t0, t_end);
         else
-            store_rows<SWZ, true>(dst, nrm, norm_mask, t0, t_end);
+            store_rows<SWZ, true, NEG_TAIL>(dst, nrm, norm_mask, t0, t_end);
     }
-    template <bool SWZ, bool MASK>
-    __device__ __forceinline__ void store_rows(T* const* dst, float* nrm, int norm_mask, int t0, int t_end) const {
+    template <bool SWZ, bool MASK, bool NEG_TAIL = false>
+    __device__ __forceinline__ void store_rows(Ptrs<T*> dst, float* nrm, int norm_mask, int t0, int t_end) const {
         constexpr int RS = LdsTile<T, D>::RS;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -171,18 +183,17 @@ struct Prefetch {
                 const int row = cc / CPR, col = 8 * (cc % CPR);
                 vec8<T> x = v[i];
                 if (MASK && t0 + row >= t_end) x = zero8<T>();
-                // a select over constant indices (not dst[tn]) keeps the LDS
-                // address space visible to the compiler: no flat stores
-                T* d = dst[0];
-#pragma unroll
-                for (int u = 1; u < NTEN; ++u) d = (tn == u) ? dst[u] : d;
+                // a select between registers (not an indexed array) also
+                // keeps the LDS address space visible: no flat stores
+                T* d = dst.at(tn);
                 int off = row * RS + col;
                 if constexpr (SWZ) off = swz_tile(row, col);
                 *reinterpret_cast<vec8<T>*>(d + off) = x;
                 if ((norm_mask >> tn) & 1) {
                     float ss = sumsq8(x);
                     ss = group_sum<CPR>(ss);
-                    if (col == 0) nrm[tn * ROWS + row] = -0.5f * kLog2e * ss;
+                    if (col == 0)
+                        nrm[tn * ROWS + row] = (NEG_TAIL && MASK && t0 + row >= t_end) ? kNegInf : -0.5f * kLog2e * ss;
                 }
             }
         }
@@ -280,7 +291,7 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
         for (int nt = 0; nt < NT; ++nt) kv[ft][nt] = f4splat(0.0f);
     float M = 0.0f;
 
-    const T* src[2] = {k + xbase, v + xbase};
+    const Ptrs<const T*> src{k + xbase, v + xbase, v + xbase};
     // lane part of the transpose-read addresses of the V tiles: each read is
     // then the step's slot base plus this offset plus a constant
     const int voff = kappa_lane_off(lane, [](int row, int col) { return row * RS + col; });
@@ -291,26 +302,30 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
 #pragma unroll
     for (int u = 0; u < PD; ++u) pf[u].load(src, t_begin + ST * min(u, nsteps - 1), L - 1);
 
+    // rows past the segment's end are staged as zeros with the row constant
+    // -inf, so their features are 0 without a per-step test
     auto stage = [&](Prefetch<T, D, 512, 2, ST>& pr, int step) {
         const int sl = step % 3;
-        T* dst[2] = {tiles[sl][0], tiles[sl][1]};
-        pr.store(dst, norms[sl], 1, t_begin + ST * min(step, nsteps - 1), step < nsteps ? t_end : -1);
+        const Ptrs<T*> dst{tiles[sl][0], tiles[sl][1], tiles[sl][1]};
+        pr.template store<false, true>(dst, norms[sl], 1, t_begin + ST * min(step, nsteps - 1),
+                                       step < nsteps ? t_end : -1);
         pr.load(src, t_begin + ST * min(step + PD, nsteps - 1), L - 1);
     };
-    // projection of one step (p = exponent - M) and its lane-local maximum
+    // projection of one step (p = exponent - M) and its lane-local maximum;
+    // branch-free, so that a whole step is one block for the scheduler
     auto project = [&](int step, f4 (&p)[4][NFT]) -> float {
         const int sl = step % 3;
-        const int t0 = t_begin + ST * step;
-        const bool full = t0 + ST <= t_end;
         const T* kt = tiles[sl][0];
         float lm = kNegInf;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            f4 init = RELU ? f4splat(0.0f) : *reinterpret_cast<const f4*>(&norms[sl][16 * tt + 4 * g]) - M;
-            if (!full) {
+            const f4 nr = *reinterpret_cast<const f4*>(&norms[sl][16 * tt + 4 * g]);
+            f4 init;
+            if constexpr (RELU) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (t0 + 16 * tt + 4 * g + i >= t_end) init[i] = kNegInf;
+                for (int i = 0; i < 4; ++i) init[i] = nr[i] == kNegInf ? kNegInf : 0.0f;
+            } else {
+                init = nr - M;
             }
             vec8<T> x[KSD];
 #pragma unroll
@@ -378,9 +393,10 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
                         }
                         a[ks2][ft] = pack8t<T>(e0, e1);
                     }
-                float lm = kNegInf;
+                // the next step's projection (on the last step the same step
+                // again, unused: no branch in the step)
                 const bool more = it + 1 < nsteps;
-                if (more) lm = project(it + 1, pn);
+                const float lm = project(more ? it + 1 : it, pn);
                 const T* vt = tiles[it % 3][1];
                 // the lane offset passes through an empty asm statement, so
                 // the compiler cannot hoist (offset + constant) pairs out of
@@ -854,7 +870,7 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
     T* ptw = pt_all + (size_t)w * PTL::ELEMS;
 
     // prefetch the first chunks (K, Q, V); loads past the last chunk re-read it
-    const T* src[3] = {k + xbase, q + xbase, v + xbase};
+    const Ptrs<const T*> src{k + xbase, q + xbase, v + xbase};
     Prefetch<T, D, 64 * W, 3> pf[PD];
 #pragma unroll
     for (int u = 0; u < PD; ++u) pf[u].load(src, t_begin + 32 * min(u, nchunks - 1), L - 1);
@@ -899,7 +915,7 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
             T* vt = qt + TL::ELEMS;
             float* nrm = nrm_all + slot * 64;  // [K rows, Q rows]
             {
-                T* dst[3] = {kt, qt, vt};
+                const Ptrs<T*> dst{kt, qt, vt};
                 pf[u].store(dst, nrm, 3, t_begin + 32 * min(ci, nchunks - 1), ci < nchunks ? t_end : -1);
             }
             pf[u].load(src, t_begin + 32 * min(ci + PD, nchunks - 1), L - 1);
@@ -1119,7 +1135,7 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
     const int t_end = min(L, t_begin + seg_len);
     const int nch = (t_end - t_begin + 63) / 64;
     const size_t xbase = (size_t)bh * L * D;
-    const bf16* src[3] = {k + xbase, q + xbase, v + xbase};
+    const Ptrs<const bf16*> src{k + xbase, q + xbase, v + xbase};
 
     // projection operands of this head straight into LDS (complete before
     // the first barrier)
@@ -1168,7 +1184,7 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
         // past the last chunk: rows of the last chunk, zeroed, into the V
         // buffer the last chunk does not use
         const int cc = min(ci, nch - 1);
-        bf16* dst[3] = {tk, tq, tv0 + (size_t)(ci & 1) * SM::TILE};
+        const Ptrs<bf16*> dst{tk, tq, tv0 + (size_t)(ci & 1) * SM::TILE};
         pf.template store<true>(dst, nrm, 3, t_begin + 64 * cc, ci < nch ? t_end : -1);
     };
     auto prefetch_chunk = [&](int ci) { pf.load(src, t_begin + 64 * min(ci, nch - 1), L - 1); };
@@ -1545,7 +1561,7 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
     const int nch = (t_end - t_begin + 31) / 32;
     if (nch <= 0) return;  // workgroup-uniform
     const size_t xbase = (size_t)bh * L * D;
-    const bf16* src[3] = {k + xbase, q + xbase, v + xbase};
+    const Ptrs<const bf16*> src{k + xbase, q + xbase, v + xbase};
 
     // chunk 0 into registers first (latency overlaps the loads below)
     Prefetch<bf16, D, 512, 3, 32> pf;
@@ -1587,7 +1603,7 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
 
     auto stage_chunk = [&](int ci) {
         const int cc = min(ci, nch - 1);
-        bf16* dst[3] = {tk, tq, tv0 + (size_t)(ci & 1) * SM::TILE};
+        const Ptrs<bf16*> dst{tk, tq, tv0 + (size_t)(ci & 1) * SM::TILE};
         pf.store(dst, nrm, 1, t_begin + 32 * cc, ci < nch ? t_end : -1);
         pf.load(src, t_begin + 32 * min(ci + 1, nch - 1), L - 1);
     };
@@ -1848,7 +1864,14 @@ template <typename T, int D, int FW, int W, bool RELU>
 static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long long om_head_vecs, const T* q,
                                 const T* k, const T* v, T* out) {
     constexpr bool OM_REGS = FW * D <= 64 * 64;
-    constexpr int PD = D <= 64 ? 4 : (FW >= 128 ? 1 : 2);
+    // chunks in flight: as many as fit in a register budget per thread (a
+    // 32-token chunk of q, k, v is spread over the workgroup's threads); 48
+    // registers, 16 for fp32 with eight waves (two waves per SIMD share its
+    // registers, and fp32 operands take twice the registers of bf16 ones)
+    constexpr int PER = (32 * (D / 8) * 3 + 64 * W - 1) / (64 * W);
+    constexpr int REGS = PER * (int)sizeof(vec8<T>) / 4;
+    constexpr int BUDGET = (sizeof(T) == 4 && W >= 8) ? 16 : 48;
+    constexpr int PD = REGS >= BUDGET ? 1 : (BUDGET / REGS > 4 ? 4 : BUDGET / REGS);
     constexpr size_t two = CausalSmem<T, D, FW, W, 2>::BYTES;
     const dim3 grid(a.nseg, a.B * a.H), block(64 * W);
     if constexpr (two <= kMaxLds) {
@@ -1990,16 +2013,23 @@ static hipError_t launch_all(const LaunchArgs& a) {
             return err;
         }
     }
-    const CausalCfg cfg = causal_config(D, a.m);
+    // the feature-split scan; only the (features per wave, waves) pairs that
+    // causal_config can return for this element type and d are instantiated
+    const CausalCfg cfg = causal_config((int)sizeof(T), D, a.m);
     hipError_t err = hipErrorInvalidValue;
+    constexpr bool narrow = (sizeof(T) == 2 && D == 128) || (sizeof(T) == 4 && D == 64);
     if (cfg.fw == 32 && cfg.w == 1) err = launch_causal<T, D, 32, 1, RELU>(a, ompack, om_head_vecs, q, k, v, out);
-    else if (cfg.fw == 64 && cfg.w == 1) err = launch_causal<T, D, 64, 1, RELU>(a, ompack, om_head_vecs, q, k, v, out);
-    else if (cfg.fw == 64 && cfg.w == 2) err = launch_causal<T, D, 64, 2, RELU>(a, ompack, om_head_vecs, q, k, v, out);
-    else if (cfg.fw == 64 && cfg.w == 4) err = launch_causal<T, D, 64, 4, RELU>(a, ompack, om_head_vecs, q, k, v, out);
-    else if constexpr (D <= 64) {
-        if (cfg.fw == 64 && cfg.w == 8) err = launch_causal<T, D, 64, 8, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+    if constexpr (narrow) {
+        if (cfg.fw == 32 && cfg.w == 2) err = launch_causal<T, D, 32, 2, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+        else if (cfg.fw == 32 && cfg.w == 4) err = launch_causal<T, D, 32, 4, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+        if constexpr (sizeof(T) == 4) {  // m = 256 (bf16, d = 128, runs the column-half scan)
+            if (cfg.fw == 32 && cfg.w == 8) err = launch_causal<T, D, 32, 8, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+        }
     } else {
-        if (cfg.fw == 128 && cfg.w == 4) err = launch_causal<T, D, 128, 4, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+        if (cfg.fw == 64 && cfg.w == 1) err = launch_causal<T, D, 64, 1, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+        else if (cfg.fw == 64 && cfg.w == 2) err = launch_causal<T, D, 64, 2, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+        else if (cfg.fw == 64 && cfg.w == 4) err = launch_causal<T, D, 64, 4, RELU>(a, ompack, om_head_vecs, q, k, v, out);
+        else if (cfg.fw == 64 && cfg.w == 8) err = launch_causal<T, D, 64, 8, RELU>(a, ompack, om_head_vecs, q, k, v, out);
     }
     stage_event(a, 3);
     return err;

@@ -9,23 +9,31 @@ int causal_chunk_tokens(int dtype_bytes, int D, int m) {
     return (dtype_bytes == 2 && D == 64 && (m == 64 || m == 128 || m == 256)) ? 64 : 32;
 }
 
-CausalCfg causal_config(int D, int m) {
-    // Features per wave (fw) and waves (w = m / fw): the wave's state slice
-    // fw x (D + 16) fp32 lives in registers.
+bool causal_wide_shape(int dtype_bytes, int D, int m) { return dtype_bytes == 2 && D == 128 && (m == 256 || m == 512); }
+
+CausalCfg causal_config(int dtype_bytes, int D, int m) {
+    // The feature-split scan: features per wave (fw) and waves (w = m / fw).
+    // A wave keeps its state slice fw x (D + 1) fp32 and its projection
+    // operands in registers; where 64 features of that would not fit beside
+    // the tiles in flight (bf16 with d = 128, fp32 with d = 64), waves take
+    // 32 features each.
     CausalCfg c{0, 0, 0};
+    const bool narrow = (dtype_bytes == 2 && D == 128) || (dtype_bytes == 4 && D == 64);
     if (m == 32) {
         c = CausalCfg{32, 1, 1};
-    } else if (m == 64 || m == 128 || m == 256) {
+    } else if (narrow && (m == 64 || m == 128 || m == 256)) {
+        c = CausalCfg{32, m / 32, m / 32};
+    } else if (!narrow && (m == 64 || m == 128 || m == 256 || m == 512)) {
         c = CausalCfg{64, m / 64, m / 64};
-    } else if (m == 512) {
-        c = D <= 64 ? CausalCfg{64, 8, 8} : CausalCfg{128, 4, 4};
     }
     return c;
 }
 
 size_t causal_smem_bytes(int dtype_bytes, int D, int m) {
-    // Same layout as CausalSmem with one partial buffer (the smallest form).
-    const CausalCfg c = causal_config(D, m);
+    // the d = 128 scan of its own (bf16, m in {256, 512}) fits by construction
+    if (causal_wide_shape(dtype_bytes, D, m)) return 0;
+    // The feature-split scan with one partial buffer (its smallest form).
+    const CausalCfg c = causal_config(dtype_bytes, D, m);
     if (c.w == 0 || (dtype_bytes == 4 && D >= 128)) return ~(size_t)0;
     const size_t eb = (size_t)dtype_bytes;
     const size_t stage = 3 * 32 * (size_t)(D + 16 / dtype_bytes);
