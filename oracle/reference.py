@@ -41,6 +41,11 @@ Readings where the pages leave a step open:
   marginally N(0, I_d); ceil(m/d) independent blocks are stacked and the last
   is cut to the rows needed ([P1] core components and atomic insights:
   block-wise orthogonalisation when r > d; [P3] A.2: marginals preserved).
+* Structured orthogonal blocks: the pages name Hadamard and Givens ORFs as
+  cheaper variants with a small bias that vanishes as d grows ([P3] A.2 ORF
+  bullet, B.3) and print neither construction.  Hadamard: sqrt(d) H S1 H S2
+  H S3 (hadamard_omega).  Givens: a product of d ceil(log2 d) random plane
+  rotations of the identity, rows scaled to chi(d) lengths (givens_omega).
 * Generalised (ReLU) features: the pages name Performer-ReLU as FAVOR+ with
   another kernel function ([P1] Digest; [P3] section 2) without printing its
   map; the reading taken is phi(x)_i = m^-1/2 max(omega_i . x, 0), the same
@@ -246,6 +251,83 @@ def hadamard_omega(seed: int, n_heads: int, m: int, d: int) -> np.ndarray:
             blk = hadamard_block_from_signs(hadamard_signs(seed, b, h, d))
             rows = min(d, m - b * d)
             out[h, b * d: b * d + rows] = blk[:rows].astype(np.float32)
+    return out
+
+
+def givens_default_rotations(d: int) -> int:
+    """Default number of rotations per block: d * ceil(log2 d), the order of
+    steps after which a walk of random plane rotations on d coordinates is
+    close to a uniformly random rotation."""
+    return d * max(1, int(np.ceil(np.log2(d))))
+
+
+def givens_rotations(seed: int, block: int, head: int, d: int, count: int):
+    """Plane rotations of one block, in the order they are applied.
+
+    Rotation k reads Philox4x64-10 with key (seed, 0) and counter
+    (k, block, head, 5); of its output words w0, w1, w2:
+      i  = floor(d * (w0 >> 32) / 2^32),
+      j' = floor((d - 1) * (w1 >> 32) / 2^32), j = j' + (j' >= i)  (so j != i,
+           uniform over the other d - 1 coordinates),
+      theta = 2 pi u, u = ((w2 >> 11) + 1) 2^-53.
+    Returns (i, j, theta) arrays of length ``count``.
+    """
+    if count == 0:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64), np.zeros(0)
+    ctr = np.zeros((count, 4), dtype=np.uint64)
+    ctr[:, 0] = np.arange(count, dtype=np.uint64)
+    ctr[:, 1] = np.uint64(block)
+    ctr[:, 2] = np.uint64(head)
+    ctr[:, 3] = np.uint64(5)
+    w = philox4x64_10(ctr, (seed, 0))
+    hi0 = (w[:, 0] >> np.uint64(32)).astype(object)
+    hi1 = (w[:, 1] >> np.uint64(32)).astype(object)
+    i = np.array([(d * int(a)) >> 32 for a in hi0], dtype=np.int64)
+    jp = np.array([((d - 1) * int(a)) >> 32 for a in hi1], dtype=np.int64)
+    j = jp + (jp >= i)
+    theta = 2.0 * np.pi * (((w[:, 2] >> np.uint64(11)).astype(np.float64) + 1.0) * 2.0 ** -53)
+    return i, j, theta
+
+
+def givens_block(i: np.ndarray, j: np.ndarray, theta: np.ndarray, d: int) -> np.ndarray:
+    """Product of plane rotations G_{K-1} ... G_1 G_0 (G_0 applied first) as
+    a d x d matrix.  G_k is the identity except in rows/columns (i_k, j_k):
+    [[cos, -sin], [sin, cos]], so left-multiplying mixes rows i_k and j_k."""
+    qm = np.eye(d)
+    for a, b, t in zip(i, j, theta):
+        c, s = np.cos(t), np.sin(t)
+        ra, rb = qm[a].copy(), qm[b].copy()
+        qm[a] = c * ra - s * rb
+        qm[b] = s * ra + c * rb
+    return qm
+
+
+def givens_omega(seed: int, n_heads: int, m: int, d: int, rotations: int = 0) -> np.ndarray:
+    """Structured (Givens) orthogonal projection, [n_heads, m, d] float32.
+
+    The pages name Givens ORFs beside Hadamard ones: orthogonal random
+    features that keep O(log d) random numbers per row (O(m log d) in all),
+    with a small bias that vanishes as d grows ([P3] A.2 ORF bullet, B.3
+    space/time trade-offs), without printing a construction.  The reading
+    taken: each d x d block is a product of ``rotations`` random plane
+    rotations (d ceil(log2 d) when 0) applied to the identity
+    (givens_rotations for the draws, givens_block for the order), and row i
+    of the block is scaled to the length of an independent N(0, I_d) vector
+    (the same chi(d) lengths as orf_omega: normals i*d .. i*d+d-1 of Philox
+    stream (block, head, 1)).  ceil(m/d) independent blocks per head, the
+    last cut to the rows needed.
+    """
+    if rotations < 0:
+        raise ValueError("rotations must be >= 0")
+    count = givens_default_rotations(d) if rotations == 0 else int(rotations)
+    nb = (m + d - 1) // d
+    out = np.empty((n_heads, m, d), dtype=np.float32)
+    for h in range(n_heads):
+        for b in range(nb):
+            qm = givens_block(*givens_rotations(seed, b, h, d, count), d)
+            lens = np.sqrt(np.sum(philox_normals(seed, (b, h, 1), d * d).reshape(d, d) ** 2, axis=1))
+            rows = min(d, m - b * d)
+            out[h, b * d: b * d + rows] = (qm * lens[:, None])[:rows].astype(np.float32)
     return out
 
 

@@ -530,6 +530,100 @@ def test_hadamard_signs_balanced_and_seeded():
 
 
 # ---------------------------------------------------------------------------
+# structured (Givens) orthogonal projections
+# ---------------------------------------------------------------------------
+
+def test_givens_block_special_cases():
+    """No rotation gives the identity; in the plane (d = 2) any product of
+    rotations is a rotation [[c, -s], [s, c]] with c^2 + s^2 = 1 and
+    determinant +1 (a reflection or a transposed entry fails)."""
+    i, j, t = ref.givens_rotations(4, 0, 0, 8, 0)
+    np.testing.assert_array_equal(ref.givens_block(i, j, t, 8), np.eye(8))
+    for count in (1, 2, 7):
+        q = ref.givens_block(*ref.givens_rotations(5, 1, 2, 2, count), 2)
+        assert q[0, 0] == pytest.approx(q[1, 1], abs=1e-15)
+        assert q[0, 1] == pytest.approx(-q[1, 0], abs=1e-15)
+        assert np.linalg.det(q) == pytest.approx(1.0, abs=1e-14)
+
+
+@pytest.mark.parametrize("d", [5, 16, 64])
+def test_givens_block_is_rotation(d):
+    """Any count of plane rotations gives an orthogonal matrix of
+    determinant +1 (d need not be a power of two)."""
+    q = ref.givens_block(*ref.givens_rotations(9, 0, 1, d, ref.givens_default_rotations(d)), d)
+    np.testing.assert_allclose(q @ q.T, np.eye(d), atol=1e-13)
+    assert np.linalg.det(q) == pytest.approx(1.0, abs=1e-10)
+
+
+def test_givens_draws_uniform():
+    """Coordinate pairs are uniform over the 12 ordered pairs of d = 4 with
+    i != j (chi-square at 11 degrees of freedom, p > 1e-4) and angles are
+    uniform on (0, 2 pi] (Kolmogorov-Smirnov, p > 1e-4)."""
+    from scipy import stats
+    i, j, t = ref.givens_rotations(1, 0, 0, 4, 24000)
+    assert np.all(i != j) and i.min() >= 0 and j.max() <= 3
+    counts = np.bincount(i * 4 + j, minlength=16)[[a * 4 + b for a in range(4) for b in range(4) if a != b]]
+    assert stats.chisquare(counts).pvalue > 1e-4
+    assert np.all((t > 0) & (t <= 2 * np.pi))
+    assert stats.kstest(t / (2 * np.pi), "uniform").pvalue > 1e-4
+
+
+def test_givens_mixing_toward_uniform_rotation():
+    """A row of a uniformly random rotation has E[u_c^2] = 1/d in every
+    coordinate.  Over 300 seeds at d = 16 the default 64 rotations bring
+    every coordinate's mean within 5 standard errors of 1/d, while 2 or 16
+    rotations leave the row near its starting axis (the statistic has the
+    power to tell), and the starting coordinate's excess shrinks as the
+    count grows."""
+    d = 16
+
+    def stats_for(count):
+        c = np.array([ref.givens_block(*ref.givens_rotations(s, 0, 0, d, count), d)[0] ** 2 for s in range(300)])
+        z = (c.mean(0) - 1.0 / d) / (c.std(0, ddof=1) / np.sqrt(len(c)))
+        return float(np.abs(z).max()), float(c.mean(0)[0] - 1.0 / d)
+
+    z2, e2 = stats_for(2)
+    z16, e16 = stats_for(16)
+    z64, e64 = stats_for(ref.givens_default_rotations(d))
+    assert ref.givens_default_rotations(d) == 64
+    assert z64 <= 5.0
+    assert z2 > 20.0 and z16 > 8.0
+    assert e2 > e16 > e64 > -0.01
+
+
+def test_givens_omega_rows_orthogonal_with_chi_lengths():
+    """Rows of a block are orthogonal, and row i of block b has the length
+    the Gram-Schmidt construction gives the same row (both take chi(d)
+    lengths from Philox stream (b, h, 1)); the last block is cut to m."""
+    seed, H, m, d = 3, 2, 40, 16
+    om = ref.givens_omega(seed, H, m, d).astype(np.float64)
+    orf = ref.orf_omega(seed, H, m, d).astype(np.float64)
+    np.testing.assert_allclose(np.linalg.norm(om, axis=-1), np.linalg.norm(orf, axis=-1), rtol=1e-6)
+    for h in range(H):
+        for b in range((m + d - 1) // d):
+            blk = om[h, b * d: min(m, (b + 1) * d)]
+            g = blk @ blk.T
+            off = g - np.diag(np.diag(g))
+            assert np.abs(off).max() <= 1e-5 * np.diag(g).max()
+    assert not np.array_equal(ref.givens_omega(1, 1, 32, 16), ref.givens_omega(2, 1, 32, 16))
+
+
+def test_givens_features_nearly_unbiased():
+    """Theorem 1 with a Givens projection: over 3000 seeds (m = d = 16,
+    small |x|, |y|) the mean estimate is within 5 standard errors of
+    exp(x.y); the pages state a small bias that vanishes as d grows, and
+    here it is below the Monte-Carlo resolution."""
+    rng = _rng(77)
+    d = 16
+    x = rng.normal(size=d) * 0.25
+    y = rng.normal(size=d) * 0.25
+    sm = np.exp(x @ y)
+    e = np.array([ref.sm_hat(x, y, ref.givens_omega(s, 1, d, d)[0].astype(np.float64)) for s in range(3000)])
+    se = e.std(ddof=1) / np.sqrt(len(e))
+    assert abs(e.mean() - sm) <= 5 * se
+
+
+# ---------------------------------------------------------------------------
 # trigonometric features (the estimator the approximation study compares with)
 # ---------------------------------------------------------------------------
 
