@@ -270,6 +270,28 @@ favor_status favor_orf_omega(unsigned long long seed, int n_heads, int m, int d,
 favor_status favor_hadamard_omega(unsigned long long seed, int n_heads, int m, int d, float *omega,
                                   void *stream);
 
+/*
+ * Structured (Givens) orthogonal projection generated on the DEVICE:
+ * omega[n_heads, m, d] (fp32, device memory, 16-byte aligned), enqueued on
+ * `stream`.  Givens ORFs keep O(m log d) random numbers and carry a small
+ * bias that vanishes as d grows (paperlayer.ai summary, A.2 ORF bullet and
+ * B.3 trade-offs; the pages print no construction).  Each d x d block is the
+ * product G_{K-1} ... G_1 G_0 of K plane rotations applied to the identity
+ * (K = rotations, or d * ceil(log2 d) when rotations = 0); G_k acts on rows
+ * (i_k, j_k) as [[cos t_k, -sin t_k], [sin t_k, cos t_k]].  Row r of a block
+ * is then scaled to the chi(d) length favor_orf_omega gives row r of the same
+ * block.  Rotation k of block b of head h: Philox4x64-10 with key (seed, 0)
+ * and counter (k, b, h, 5), output words w0..w2:
+ * i = floor(d (w0 >> 32) / 2^32), j' = floor((d - 1) (w1 >> 32) / 2^32),
+ * j = j' + (j' >= i), t = 2 pi ((w2 >> 11) + 1) 2^-53.  Computed in fp64 and
+ * rounded to fp32 once.  ceil(m/d) blocks per head, the last cut to the rows
+ * needed.  2 <= d <= 128, n_heads <= 65535 and n_heads * m * d < 2^31 (else
+ * FAVOR_ERR_UNSUPPORTED); null or misaligned omega, n_heads < 1, m < 1 or
+ * rotations outside [0, 2^24]: FAVOR_ERR_INVALID_ARG.
+ */
+favor_status favor_givens_omega(unsigned long long seed, int n_heads, int m, int d, int rotations, float *omega,
+                                void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *favor_status_string(favor_status status);
 

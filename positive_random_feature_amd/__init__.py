@@ -14,7 +14,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["features", "bidir", "causal", "causal_noalloc", "orf_omega", "hadamard_omega", "workspace_bytes", "state_floats",
+__all__ = ["features", "bidir", "causal", "causal_noalloc", "orf_omega", "hadamard_omega", "givens_omega", "workspace_bytes", "state_floats",
            "state_parts", "FavorError"]
 
 FavorError = _lib.FavorError
@@ -224,4 +224,16 @@ def hadamard_omega(seed: int, n_heads: int, m: int, d: int, device="cuda") -> to
     out = torch.empty((n_heads, m, d), dtype=torch.float32, device=dev)
     st = _lib.load().favor_hadamard_omega(int(seed), int(n_heads), int(m), int(d), out.data_ptr(), _stream(dev))
     _lib.check(st, "favor_hadamard_omega")
+    return out
+
+
+def givens_omega(seed: int, n_heads: int, m: int, d: int, rotations: int = 0, device="cuda") -> torch.Tensor:
+    """Structured (Givens) orthogonal projection [n_heads, m, d] (float32),
+    generated on the device: each block a product of random plane rotations
+    (d ceil(log2 d) of them when ``rotations`` is 0) with chi(d) row lengths."""
+    dev = torch.device(device)
+    out = torch.empty((n_heads, m, d), dtype=torch.float32, device=dev)
+    st = _lib.load().favor_givens_omega(int(seed), int(n_heads), int(m), int(d), int(rotations), out.data_ptr(),
+                                        _stream(dev))
+    _lib.check(st, "favor_givens_omega")
     return out

@@ -87,6 +87,9 @@ def load() -> ctypes.CDLL:
     lib.favor_orf_omega.argtypes = [ctypes.c_ulonglong, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.favor_hadamard_omega.restype = ctypes.c_int
     lib.favor_hadamard_omega.argtypes = [ctypes.c_ulonglong, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.favor_givens_omega.restype = ctypes.c_int
+    lib.favor_givens_omega.argtypes = [ctypes.c_ulonglong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                       vp]
     lib.favor_status_string.restype = ctypes.c_char_p
     lib.favor_status_string.argtypes = [ctypes.c_int]
     _lib = lib

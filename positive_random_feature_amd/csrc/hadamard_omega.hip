@@ -15,35 +15,15 @@
 // (seed, 0); diagonal t of block b of head h reads counter (0, b, h, 2 + t),
 // entry j is -1 when bit j % 64 of output word j / 64 is set.
 #include "../../include/favor.h"
+#include "philox_device.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace {
 
-struct Words {
-    uint64_t w[4];
-};
-
-__device__ Words philox4x64_10(Words c, uint64_t k0, uint64_t k1) {
-    const uint64_t M0 = 0xD2E7470EE14C6C93ULL, M1 = 0xCA5A826395121157ULL;
-    const uint64_t W0 = 0x9E3779B97F4A7C15ULL, W1 = 0xBB67AE8584CAA73BULL;
-    for (int round = 0; round < 10; ++round) {
-        if (round > 0) {
-            k0 += W0;
-            k1 += W1;
-        }
-        const uint64_t hi0 = __umul64hi(M0, c.w[0]), lo0 = M0 * c.w[0];
-        const uint64_t hi1 = __umul64hi(M1, c.w[2]), lo1 = M1 * c.w[2];
-        Words n;
-        n.w[0] = hi1 ^ c.w[1] ^ k0;
-        n.w[1] = lo1;
-        n.w[2] = hi0 ^ c.w[3] ^ k1;
-        n.w[3] = lo0;
-        c = n;
-    }
-    return c;
-}
+using favor_rng::Words;
+using favor_rng::philox4x64_10;
 
 // Unnormalised Walsh-Hadamard transform of a row vector, in place (the
 // Sylvester matrix is symmetric, so v H = H v).

@@ -220,6 +220,20 @@ def test_hadamard_omega_validation(lib):
     assert f(0, 1 << 12, 1 << 12, 128, P_OM, None) == UNSUPPORTED  # >= 2^31 elements
 
 
+def test_givens_omega_validation(lib):
+    f = lib.favor_givens_omega
+    assert f(0, 1, 32, 16, 0, None, None) == INVALID
+    assert f(0, 1, 32, 16, 0, P_OM + 4, None) == INVALID    # 16-byte alignment
+    assert f(0, 0, 32, 16, 0, P_OM, None) == INVALID
+    assert f(0, 1, 0, 16, 0, P_OM, None) == INVALID
+    assert f(0, 1, 32, 16, -1, P_OM, None) == INVALID       # rotations in [0, 2^24]
+    assert f(0, 1, 32, 16, (1 << 24) + 1, P_OM, None) == INVALID
+    assert f(0, 1, 32, 1, 0, P_OM, None) == UNSUPPORTED     # 2 <= d <= 128
+    assert f(0, 1, 32, 129, 0, P_OM, None) == UNSUPPORTED
+    assert f(0, 65536, 1, 16, 0, P_OM, None) == UNSUPPORTED  # one grid row per head
+    assert f(0, 1 << 12, 1 << 12, 128, 0, P_OM, None) == UNSUPPORTED  # >= 2^31 elements
+
+
 def _causal_plan(lib, s, chunk=0, segments=0, ws=P_WS, nbytes=1 << 40):
     pl = _lib.plan(chunk, segments)
     return lib.favor_causal_plan(ctypes.byref(s), P_Q, P_K, P_V, P_OM, P_O, ctypes.byref(pl), ws, nbytes, None)

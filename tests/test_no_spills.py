@@ -32,7 +32,7 @@ def _resource_usage(source):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="no hipcc")
-@pytest.mark.parametrize("source,at_least", [("favor_kernels.hip", 150), ("hadamard_omega.hip", 4)])
+@pytest.mark.parametrize("source,at_least", [("favor_kernels.hip", 150), ("hadamard_omega.hip", 4), ("givens_omega.hip", 1)])
 def test_no_scratch(source, at_least):
     kernels = _resource_usage(source)
     assert len(kernels) >= at_least, len(kernels)
