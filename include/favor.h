@@ -105,6 +105,22 @@ favor_status favor_features(const favor_shape *shape, const void *x, const float
                             float *log_scale, int stabilize, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * favor_features over the structured Hadamard projection that
+ * favor_hadamard_omega(seed, n, m, d) would generate (n = H when
+ * shape->omega_head_stride != 0, one set of blocks per head; else the blocks
+ * of head 0 for every head), without materialising it: the blocks
+ * sqrt(d) H S1 H S2 H S3 are applied to x as three fast Walsh-Hadamard
+ * transforms with sign flips, d log2 d additions each instead of a dense
+ * d x d product (paperlayer.ai summary, B.3: structured projections build
+ * the features in O(L m log d)).  The signs are drawn from the seed inside
+ * the call; no workspace, and the projection is exact in fp32 (no rounding
+ * of omega to the input dtype).  Same shapes, outputs, stabiliser and
+ * overlap rules as favor_features (x, phi, log_scale); B * H <= 65535.
+ */
+favor_status favor_features_hadamard(const favor_shape *shape, const void *x, unsigned long long seed, float *phi,
+                                     float *log_scale, int stabilize, void *stream);
+
+/*
  * Bidirectional FAVOR+ ("Performer" digest, key formulas and method
  * flowchart):
  *     out_t = phi(q_t)^T (sum_s phi(k_s) v_s^T) / phi(q_t)^T (sum_s phi(k_s)).

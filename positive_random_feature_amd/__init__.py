@@ -14,7 +14,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["features", "bidir", "causal", "causal_noalloc", "orf_omega", "hadamard_omega", "givens_omega", "workspace_bytes", "state_floats",
+__all__ = ["features", "features_hadamard", "bidir", "causal", "causal_noalloc", "orf_omega", "hadamard_omega", "givens_omega", "workspace_bytes", "state_floats",
            "state_parts", "FavorError"]
 
 FavorError = _lib.FavorError
@@ -119,6 +119,32 @@ def features(x: torch.Tensor, omega: torch.Tensor, stabilize: bool = False, feat
                                     log_scale.data_ptr() if stabilize else None, 1 if stabilize else 0,
                                     ws.data_ptr(), ws.numel(), _stream(dev))
     _lib.check(st, "favor_features")
+    return phi, log_scale
+
+
+def features_hadamard(x: torch.Tensor, seed: int, m: int, per_head: bool = True, stabilize: bool = False,
+                      feature: str = "positive"):
+    """``features`` over the structured Hadamard projection that
+    ``hadamard_omega(seed, H if per_head else 1, m, d)`` would generate, built
+    with fast Walsh-Hadamard transforms instead of a dense projection (the
+    projection itself is never formed).  Returns (phi, log_scale or None)."""
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    if x.dim() != 4 or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous [B, H, L, d] tensor; got {tuple(x.shape)}")
+    if feature not in _FEATURES:
+        raise ValueError(f"feature must be one of {sorted(_FEATURES)}")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be on a GPU device")
+    B, H, L, d = x.shape
+    shp = _lib.shape(B, H, L, d, int(m), _DTYPES[x.dtype], int(m) * d if per_head else 0, _FEATURES[feature])
+    phi = torch.empty((B, H, L, int(m)), dtype=torch.float32, device=dev)
+    log_scale = torch.empty((B, H, L), dtype=torch.float32, device=dev) if stabilize else None
+    st = _lib.load().favor_features_hadamard(ctypes.byref(shp), x.data_ptr(), int(seed), phi.data_ptr(),
+                                             log_scale.data_ptr() if stabilize else None, 1 if stabilize else 0,
+                                             _stream(dev))
+    _lib.check(st, "favor_features_hadamard")
     return phi, log_scale
 
 

@@ -87,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.favor_orf_omega.argtypes = [ctypes.c_ulonglong, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.favor_hadamard_omega.restype = ctypes.c_int
     lib.favor_hadamard_omega.argtypes = [ctypes.c_ulonglong, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.favor_features_hadamard.restype = ctypes.c_int
+    lib.favor_features_hadamard.argtypes = [sp, vp, ctypes.c_ulonglong, vp, vp, ctypes.c_int, vp]
     lib.favor_givens_omega.restype = ctypes.c_int
     lib.favor_givens_omega.argtypes = [ctypes.c_ulonglong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
                                        vp]

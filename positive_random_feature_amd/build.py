@@ -8,7 +8,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfavor_amd.so")
-SOURCES = ["favor_kernels.hip", "favor_api.cpp", "favor_plan.cpp", "orf_omega.cpp", "hadamard_omega.hip", "givens_omega.hip", "favor_noalloc.hip"]
+SOURCES = ["favor_kernels.hip", "favor_api.cpp", "favor_plan.cpp", "orf_omega.cpp", "hadamard_omega.hip", "givens_omega.hip", "structured_features.hip", "favor_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950",

@@ -271,6 +271,32 @@ favor_status favor_features(const favor_shape* shape, const void* x, const float
     return run(c);
 }
 
+favor_status favor_features_hadamard(const favor_shape* shape, const void* x, unsigned long long seed, float* phi,
+                                     float* log_scale, int stabilize, void* stream) {
+    const favor_shape* s = shape;
+    favor_status st = check_shape(s, FAVOR_OP_FEATURES);
+    if (st != FAVOR_OK) return st;
+    if (s->B * s->H > 65535) return FAVOR_ERR_UNSUPPORTED;  // one grid row per (batch, head)
+    if (s->L == 0) return FAVOR_OK;
+    const size_t xbytes = (size_t)s->B * s->H * s->L * s->d * dtype_bytes(s->dtype);
+    const size_t pbytes = (size_t)s->B * s->H * s->L * s->m * sizeof(float);
+    const size_t lbytes = (size_t)s->B * s->H * s->L * sizeof(float);
+    if (!x || !phi || !aligned(x, 16) || !aligned(phi, 16)) return FAVOR_ERR_INVALID_ARG;
+    if (stabilize && (!log_scale || !aligned(log_scale, 4))) return FAVOR_ERR_INVALID_ARG;
+    if (overlaps(phi, pbytes, x, xbytes)) return FAVOR_ERR_INVALID_ARG;
+    if (stabilize && (overlaps(log_scale, lbytes, phi, pbytes) || overlaps(log_scale, lbytes, x, xbytes)))
+        return FAVOR_ERR_INVALID_ARG;
+    favor::HadamardFeaturesArgs a{};
+    a.dtype_bytes = dtype_bytes(s->dtype);
+    a.B = s->B; a.H = s->H; a.L = s->L; a.D = s->d; a.m = s->m;
+    a.relu = s->feature == FAVOR_FEATURE_RELU;
+    a.omega_per_head = s->omega_head_stride != 0 ? 1 : 0;
+    a.seed = seed; a.x = x; a.phi = phi; a.log_scale = stabilize ? log_scale : nullptr;
+    a.stabilize = stabilize ? 1 : 0;
+    a.stream = static_cast<hipStream_t>(stream);
+    return favor::launch_hadamard_features(a) == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
 favor_status favor_bidir(const favor_shape* shape, const void* q, const void* k, const void* v, const float* omega,
                          void* out, void* ws, size_t ws_bytes, void* stream) {
     return run(attention(FAVOR_OP_BIDIR, shape, q, k, v, omega, out, ws, ws_bytes, stream));

@@ -55,6 +55,22 @@ struct CausalCfg {
 };
 
 hipError_t launch(const LaunchArgs& a);
+
+// Features over the structured Hadamard projection, built with fast
+// Walsh-Hadamard transforms from the seed (favor_features_hadamard).
+struct HadamardFeaturesArgs {
+    int dtype_bytes;
+    int B, H, L, D, m;
+    bool relu;
+    int omega_per_head;  // 1: the blocks of head h; 0: those of head 0 for every head
+    unsigned long long seed;
+    const void* x;
+    float* phi;
+    float* log_scale;
+    int stabilize;
+    hipStream_t stream;
+};
+hipError_t launch_hadamard_features(const HadamardFeaturesArgs& a);
 // Tokens per step of the causal chunked scan for a shape.
 int causal_chunk_tokens(int dtype_bytes, int D, int m);
 CausalCfg causal_config(int dtype_bytes, int D, int m);

@@ -220,6 +220,24 @@ def test_hadamard_omega_validation(lib):
     assert f(0, 1 << 12, 1 << 12, 128, P_OM, None) == UNSUPPORTED  # >= 2^31 elements
 
 
+def test_features_hadamard_validation(lib):
+    f = lib.favor_features_hadamard
+
+    def call(s, x=P_Q, phi=P_O, ls=None, stab=0):
+        return f(ctypes.byref(s), x, 1, phi, ls, stab, None)
+
+    assert call(shp(B=1, H=1, L=0)) == OK                 # nothing to do
+    assert f(None, P_Q, 1, P_O, None, 0, None) == INVALID
+    assert call(shp(), x=None) == INVALID
+    assert call(shp(), phi=None) == INVALID
+    assert call(shp(), x=P_Q + 8) == INVALID                 # 16-byte alignment
+    assert call(shp(), stab=1) == INVALID                     # stabilised: log_scale required
+    assert call(shp(d=48)) == UNSUPPORTED
+    assert call(shp(m=48)) == UNSUPPORTED
+    assert call(shp(B=300, H=300)) == UNSUPPORTED           # one grid row per (batch, head)
+    assert call(shp(), phi=P_Q) == INVALID                    # phi overlaps x
+
+
 def test_givens_omega_validation(lib):
     f = lib.favor_givens_omega
     assert f(0, 1, 32, 16, 0, None, None) == INVALID
