@@ -364,6 +364,64 @@ def time_hadamard(hip, dev, stream, n_heads=16, m=512, d=128, reps=50):
     return {"heads": n_heads, "m": m, "d": d, "us_per_call": us, "gbs_written": n_heads * m * d * 4 / (us * 1e-6) / 1e9}
 
 
+def time_givens(hip, dev, stream, n_heads=16, m=512, d=128, reps=20):
+    """Device generation of a structured (Givens) projection of the long
+    causal workload's size (d ceil(log2 d) rotations per block)."""
+    lib = _lib.load()
+    out = torch.empty((n_heads, m, d), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        _lib.check(lib.favor_givens_omega(1, n_heads, m, d, 0, out.data_ptr(), stream), "favor_givens_omega")
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for i in range(reps):
+        _lib.check(lib.favor_givens_omega(i, n_heads, m, d, 0, out.data_ptr(), stream), "favor_givens_omega")
+    hip.record(e1, stream)
+    us = hip.elapsed_ms(e0, e1) / reps * 1e3
+    return {"heads": n_heads, "m": m, "d": d, "us_per_call": us}
+
+
+def time_structured_features(hip, dev, stream, B=4, H=8, L=4096, reps=50):
+    """Stabilised bf16 features of B x H x L tokens (m = 4d, Hadamard
+    projection per head) two ways: the dense matrix-core projection of the
+    materialised projection (favor_features, its projection packing
+    included) and fast Walsh-Hadamard transforms from the seed
+    (favor_features_hadamard).  Both write the same fp32 features."""
+    lib = _lib.load()
+    rows = []
+    for d in (16, 32, 64, 128):
+        m = 4 * d
+        g = torch.Generator(device="cpu").manual_seed(d)
+        x = (torch.randn((B, H, L, d), generator=g) * d ** -0.25).to(torch.bfloat16).to(dev)
+        om = favor.hadamard_omega(1, H, m, d, device=dev)
+        shp = favor._shape(x, om)
+        ws = torch.empty(favor.workspace_bytes(_lib.FAVOR_OP_FEATURES, shp), dtype=torch.uint8, device=dev)
+        phi = torch.empty((B, H, L, m), dtype=torch.float32, device=dev)
+        ls = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+
+        def dense():
+            _lib.check(lib.favor_features(ctypes.byref(shp), x.data_ptr(), om.data_ptr(), phi.data_ptr(),
+                                          ls.data_ptr(), 1, ws.data_ptr(), ws.numel(), stream), "favor_features")
+
+        def fwht():
+            _lib.check(lib.favor_features_hadamard(ctypes.byref(shp), x.data_ptr(), 1, phi.data_ptr(), ls.data_ptr(),
+                                                   1, stream), "favor_features_hadamard")
+
+        res = {"d": d, "m": m, "tokens": B * H * L, "phi_bytes": B * H * L * m * 4}
+        for name, fn in (("dense_us", dense), ("fwht_us", fwht)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            for _ in range(reps):
+                fn()
+            hip.record(e1, stream)
+            res[name] = hip.elapsed_ms(e0, e1) / reps * 1e3
+        rows.append(res)
+    return rows
+
+
 def time_streaming(hip, dev, stream, name="causal_bf16_8k", pieces=8, reps=50):
     """The causal workload fed in `pieces` consecutive pieces, each call
     continuing from the previous call's carried state (favor_causal_state)."""
@@ -478,6 +536,125 @@ def summarise_counters(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+# Known-traffic runs for a per-kernel check of the HBM counters: every input
+# is far larger than the 32 MB of L2, so each kernel's L2-miss reads are its
+# input streams and its writes are its outputs.
+CALIB_SHAPES = {
+    "features": dict(B=8, H=8, L=16384, d=64, m=64),
+    "bidir": dict(B=4, H=8, L=32768, d=64, m=256),
+    "causal": dict(B=2, H=8, L=65536, d=64, m=256),
+}
+CALIB_COPY_BYTES = 512 << 20
+
+
+def calib_expected():
+    """(label, kernel, read bytes, write bytes, what) of each dispatch of the
+    --calib-kernels run, in launch order (small operand streams -- packed
+    projections, shifts -- are left out and named)."""
+    f = CALIB_SHAPES["features"]
+    x = f["B"] * f["H"] * f["L"] * f["d"] * 2
+    phi = f["B"] * f["H"] * f["L"] * f["m"] * 4
+    rows = [("features:features", "features_kernel", x, phi, "x read, phi written"),
+            ("fwht:hadamard_features", "hadamard_features_kernel", x, phi, "x read, phi written")]
+    for op in ("bidir", "causal"):
+        c = CALIB_SHAPES[op]
+        bh = c["B"] * c["H"]
+        t = bh * c["L"] * c["d"] * 2
+        nseg = -(-favor_kernels_target() // bh)
+        part = bh * nseg * c["m"] * (c["d"] + 1) * 4
+        rows.append((f"{op}:kv_partial", "kv_partial_kernel", 2 * t, part, "k, v read; segment sums written"))
+        rows.append((f"{op}:merge_scan", "merge_scan_kernel", part, 0 if op == "bidir" else part,
+                     "segment sums read" + ("" if op == "bidir" else "; carries written")))
+        if op == "bidir":
+            rows.append(("bidir:bidir_out", "bidir_out_kernel", t, t, "q read, out written"))
+        else:
+            rows.append(("causal:causal_tile", "causal_tile_kernel", 3 * t + part, t, "q, k, v, carries read; out written"))
+    rows.append(("copy", None, CALIB_COPY_BYTES, CALIB_COPY_BYTES, "device copy"))
+    return rows
+
+
+def favor_kernels_target():
+    """Workgroups the launch plan aims for (one per compute unit)."""
+    return 256
+
+
+def run_calib_kernels(dev):
+    """One call of each known-traffic kernel, then the calibration copy."""
+    g = torch.Generator(device="cpu").manual_seed(0)
+
+    def rnd(B, H, L, d):
+        return (torch.randn((B, H, L, d), generator=g) * d ** -0.25).to(torch.bfloat16).to(dev)
+
+    f = CALIB_SHAPES["features"]
+    x = rnd(f["B"], f["H"], f["L"], f["d"])
+    om = favor.hadamard_omega(1, 1, f["m"], f["d"], device=dev)[0].contiguous()
+    torch.cuda.synchronize()
+    favor.features(x, om)
+    favor.features_hadamard(x, 1, f["m"], per_head=False)
+    torch.cuda.synchronize()
+    del x
+    for op in ("bidir", "causal"):
+        c = CALIB_SHAPES[op]
+        q, k, v = (rnd(c["B"], c["H"], c["L"], c["d"]) for _ in range(3))
+        omc = favor.orf_omega(1, 1, c["m"], c["d"])[0].contiguous().to(dev)
+        torch.cuda.synchronize()
+        (favor.bidir if op == "bidir" else favor.causal)(q, k, v, omc)
+        torch.cuda.synchronize()
+        del q, k, v
+    src = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def summarise_calibration(dirs):
+    """Per-kernel table of the --calib-kernels runs: the raw read-request
+    counts and the derived FETCH_SIZE / WRITE_SIZE against each kernel's
+    known bytes."""
+    want = {"FETCH_SIZE", "WRITE_SIZE", "TCC_EA0_RDREQ_sum", "TCC_BUBBLE_sum", "TCC_EA0_RDREQ_32B_sum",
+            "TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"}
+    per = {}
+    for root in dirs:
+        rows = _read_csvs(root, "counter_collection.csv")
+        disp = {}
+        for r in rows:
+            if r.get("Counter_Name") in want:
+                d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        ordered = [disp[k] for k in sorted(disp)]
+        exp = calib_expected()
+        i = 0
+        for lab, kern, rb, wb, what in exp:
+            if kern is None:
+                cand = [d for d in ordered if "favor" not in d["name"]]
+                d = cand[-1] if cand else None
+            else:
+                d = None
+                while i < len(ordered):
+                    if kern in ordered[i]["name"]:
+                        d = ordered[i]
+                        i += 1
+                        break
+                    i += 1
+            if d is None:
+                raise SystemExit(f"{root}: no dispatch for {lab}")
+            per.setdefault(lab, {}).update({k: v for k, v in d.items() if k != "name"})
+    print("| kernel | expected read MB | FETCH_SIZE MB (ratio) | read requests | BUBBLE | 32 B | expected B/request | "
+          "expected write MB | WRITE_SIZE MB (ratio) | write requests | 64 B | what |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for lab, kern, rb, wb, what in calib_expected():
+        c = per[lab]
+        fs = c.get("FETCH_SIZE", float("nan")) * 1024
+        ws = c.get("WRITE_SIZE", float("nan")) * 1024
+        rq = c.get("TCC_EA0_RDREQ_sum", float("nan"))
+        wr = c.get("TCC_EA0_WRREQ_sum", float("nan"))
+        ratio_f = fs / rb if rb else float("nan")
+        ratio_w = ws / wb if wb else float("nan")
+        print(f"| {lab} | {rb / 1e6:.1f} | {fs / 1e6:.1f} ({ratio_f:.3f}) | {rq:.0f} | {c.get('TCC_BUBBLE_sum', float('nan')):.0f} | "
+              f"{c.get('TCC_EA0_RDREQ_32B_sum', float('nan')):.0f} | {rb / rq if rq else float('nan'):.1f} | {wb / 1e6:.1f} | "
+              f"{ws / 1e6:.1f} ({ratio_w:.3f}) | {wr:.0f} | {c.get('TCC_EA0_WRREQ_64B_sum', float('nan')):.0f} | {what} |")
+
+
 SQ_PASSES = (
     ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
      "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY"),
@@ -548,6 +725,9 @@ def main():
     ap.add_argument("--summarise-trace", metavar="TRACE_DIR")
     ap.add_argument("--summarise-sq", nargs=3, metavar=("PASS1_DIR", "PASS2_DIR", "PASS3_DIR"))
     ap.add_argument("--workload", choices=sorted(WORKLOADS), help="time one workload alone, stage by stage")
+    ap.add_argument("--calib-kernels", action="store_true",
+                    help="run the known-traffic kernel calls (for a per-kernel check of the HBM counters) and exit")
+    ap.add_argument("--summarise-calibration", nargs="+", metavar="PMC_DIR")
     args = ap.parse_args()
     if args.summarise_counters:
         summarise_counters(*args.summarise_counters)
@@ -557,6 +737,9 @@ def main():
         return
     if args.summarise_sq:
         summarise_sq(args.summarise_sq)
+        return
+    if args.summarise_calibration:
+        summarise_calibration(args.summarise_calibration)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library runs on one GPU and has no multi-GPU path.",
@@ -570,6 +753,10 @@ def main():
     hip = Hip()
     if args.workload:
         print(json.dumps(time_stages(hip, dev, args.workload, args.steps, args.warmup)), flush=True)
+        return
+    if args.calib_kernels:
+        run_calib_kernels(dev)
+        print(json.dumps({"calib_kernels": [r[0] for r in calib_expected()]}), flush=True)
         return
     ops = [Op("bidir_bf16_4k", dev), Op("causal_bf16_8k", dev)]
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -678,6 +865,8 @@ def main():
         result["configs"] = time_configs(hip, dev, stream)
         result["streaming"] = time_streaming(hip, dev, stream)
         result["hadamard_projection"] = time_hadamard(hip, dev, stream)
+        result["givens_projection"] = time_givens(hip, dev, stream)
+        result["structured_features"] = time_structured_features(hip, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(ops, dev, stream)
     print(json.dumps(result), flush=True)

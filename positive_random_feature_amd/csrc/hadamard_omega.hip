@@ -8,8 +8,11 @@
 // with H the normalised Sylvester-Hadamard matrix and S_t diagonal +-1
 // matrices; its rows are orthogonal with norm sqrt(d).  The projection is
 // materialised ([H, m, d] fp32) and used by the matrix-core projection like
-// any other: on gfx950 a dense 16x16x32 product costs less than a fast
-// Walsh-Hadamard transform in vector instructions for d <= 128.
+// any other.  favor_features_hadamard applies the same blocks as fast
+// Walsh-Hadamard transforms instead; measured on MI355X for stabilised bf16
+// features of 131072 tokens (m = 4d), the dense product is faster at d = 64
+// (about 42 against 57 us) and d = 128 (115 against 170 us), the transforms
+// only at d = 16, so the attention kernels keep the dense projection.
 //
 // Signs: Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, SC'11), key
 // (seed, 0); diagonal t of block b of head h reads counter (0, b, h, 2 + t),
