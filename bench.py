@@ -475,20 +475,23 @@ def _read_csvs(root, suffix):
 
 
 def _stage_labels(names):
-    """Label the favor kernel launches of bench runs by launch order: each
-    step (and each stage-timed step) runs the bidirectional op, then the
-    causal one, so kv_partial and merge_scan alternate between the two."""
-    seen = {"kv_partial": 0, "merge_scan": 0}
-    labels = []
+    """Label the favor kernel launches of bench runs: the output kernel names
+    its operation (bidir_out: the bidirectional workload, causal_tile: the
+    causal one), and the segment-sum and merge/scan launches belong to the
+    output kernel that follows them, whatever order the operations ran in."""
+    kinds = []
     for n in names:
-        k = next((k for k in ("kv_partial", "merge_scan", "bidir_out", "causal_tile") if k + "_kernel" in n), None)
-        if k is None:
-            labels.append(None)
-        elif k in seen:
-            labels.append(("bidir_bf16_4k" if seen[k] % 2 == 0 else "causal_bf16_8k") + ":" + k)
-            seen[k] += 1
-        else:
-            labels.append(("bidir_bf16_4k" if k == "bidir_out" else "causal_bf16_8k") + ":" + k)
+        kinds.append(next((k for k in ("kv_partial", "merge_scan", "bidir_out", "causal_tile") if k + "_kernel" in n),
+                          None))
+    labels = [None] * len(names)
+    nxt = None
+    for i in range(len(names) - 1, -1, -1):
+        k = kinds[i]
+        if k in ("bidir_out", "causal_tile"):
+            nxt = "bidir_bf16_4k" if k == "bidir_out" else "causal_bf16_8k"
+            labels[i] = nxt + ":" + k
+        elif k is not None and nxt is not None:
+            labels[i] = nxt + ":" + k
     return labels
 
 

@@ -10,9 +10,10 @@
 // materialised ([H, m, d] fp32) and used by the matrix-core projection like
 // any other.  favor_features_hadamard applies the same blocks as fast
 // Walsh-Hadamard transforms instead; measured on MI355X for stabilised bf16
-// features of 131072 tokens (m = 4d), the dense product is faster at d = 64
-// (about 42 against 57 us) and d = 128 (115 against 170 us), the transforms
-// only at d = 16, so the attention kernels keep the dense projection.
+// features of 131072 tokens (m = 4d), the dense matrix-core product is the
+// faster one at every d: 14 against 18 us at d = 16, 42 against 61 us at
+// d = 64, 128 against 178 us at d = 128.  The attention kernels keep the
+// dense projection.
 //
 // Signs: Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, SC'11), key
 // (seed, 0); diagonal t of block b of head h reads counter (0, b, h, 2 + t),
