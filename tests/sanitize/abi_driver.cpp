@@ -110,6 +110,28 @@ int main() {
         EXPECT(favor_causal_profiled(&s, fake(Q), fake(K), fake(V), (const float*)fake(OM), fake(O), 0, fake(WS),
                                      need, nullptr, ev, 3) == FAVOR_ERR_INVALID_ARG);
     }
+    // features over the Hadamard projection by transforms (no workspace)
+    for (int d : ds)
+        for (int m : ms)
+            for (int L : Ls)
+                for (int stab = 0; stab < 2; ++stab) {
+                    favor_shape s{2, 3, L, d, m, FAVOR_BF16, (long long)m * d, 0};
+                    const int before = g_launches;
+                    const favor_status st = favor_features_hadamard(&s, fake(Q), 5, (float*)fake(O),
+                                                                    stab ? (float*)fake(K) : nullptr, stab, nullptr);
+                    const bool shape_ok = (d == 16 || d == 32 || d == 64 || d == 128) && m % 32 == 0 && m <= 512 &&
+                                          (m <= 256 || m % 64 == 0);
+                    EXPECT(st == (shape_ok ? FAVOR_OK : FAVOR_ERR_UNSUPPORTED));
+                    EXPECT(g_launches == before + (shape_ok && L > 0 ? 1 : 0));
+                    ++calls;
+                }
+    {
+        favor_shape s{1, 1, 64, 64, 256, FAVOR_BF16, 0, 0};
+        EXPECT(favor_features_hadamard(&s, fake(Q), 5, (float*)fake(Q), nullptr, 0, nullptr) == FAVOR_ERR_INVALID_ARG);
+        EXPECT(favor_features_hadamard(&s, fake(Q), 5, (float*)fake(O), nullptr, 1, nullptr) == FAVOR_ERR_INVALID_ARG);
+        EXPECT(favor_features_hadamard(nullptr, fake(Q), 5, (float*)fake(O), nullptr, 0, nullptr) ==
+               FAVOR_ERR_INVALID_ARG);
+    }
     // extreme dimensions: no overflow in the size computations (UBSan)
     {
         favor_shape big{1 << 16, 1 << 8, 1 << 8, 64, 256, FAVOR_BF16, 0, 0};

@@ -61,4 +61,13 @@ hipError_t launch(const LaunchArgs& a) {
     return hipSuccess;
 }
 
+// The transform-features launch takes no workspace; the stub checks the
+// arguments the ABI forwards.
+hipError_t launch_hadamard_features(const HadamardFeaturesArgs& a) {
+    ++g_launches;
+    if (!a.x || !a.phi || a.L < 1 || a.m < 1 || (a.stabilize && !a.log_scale)) fail("bad transform-features launch");
+    if (a.D != 16 && a.D != 32 && a.D != 64 && a.D != 128) fail("bad d for the transform features");
+    return hipSuccess;
+}
+
 }  // namespace favor
