@@ -273,6 +273,20 @@ def alg_work(w):
     return flops, bytes_
 
 
+# Exponential issue rate of the chip: one v_exp_f32 per wave64 takes about
+# two fp32-FMA issue slots (measured), i.e. 32 exponentials per clock per
+# compute unit (4 SIMDs x 16 lanes / 2), at 256 compute units and 2.4 GHz.
+EXP_PEAK_PER_S = 256 * 2.4e9 * 32
+
+
+def exp_roof_us(w, feature="positive"):
+    """Diagnostic third roof: the 2m exponentials per token (q and k
+    features) at the chip's exponential issue rate; ReLU features have none."""
+    if feature == "relu":
+        return 0.0
+    return w.tokens * 2 * w.m / EXP_PEAK_PER_S * 1e6
+
+
 def time_configs(hip, dev, stream, reps_target_ms: float = 20.0):
     """Each workload on its own: per-call time (events around back-to-back
     calls on one stream) and its fraction of the binding roofline; the two
@@ -315,6 +329,7 @@ def time_configs(hip, dev, stream, reps_target_ms: float = 20.0):
                      "calls": n, "us_per_call": ms * 1e3, "tokens_per_s": w.tokens / (ms * 1e-3),
                      "alg_gflop": flops / 1e9, "alg_mb": bytes_ / 1e6, "bound": bound,
                      "roof_us": t_roof * 1e6, "frac": t_roof / (ms * 1e-3),
+                     "exp_roof_us": exp_roof_us(w, feature),
                      "achieved": (bytes_ / (ms * 1e-3) / 1e9) if bound == "hbm" else (flops / (ms * 1e-3) / 1e12),
                      "achieved_unit": "GB/s" if bound == "hbm" else "TFLOP/s"}
         del op
