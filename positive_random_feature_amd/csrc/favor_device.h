@@ -159,10 +159,13 @@ __device__ __forceinline__ float col_max(float x) {
     return __builtin_fmaxf(x, __shfl_xor(x, 32));
 }
 
-// DPP lane permutations inside rows of 16 lanes (no LDS traffic).
+// DPP lane permutations inside rows of 16 lanes (no LDS traffic).  Every
+// permutation used here gives each lane a valid source lane, so the
+// out-of-range value (bound_ctrl: zero) never appears; with no old value to
+// keep, the compiler folds the permutation into the instruction that uses it
+// (one v_add_f32_dpp / v_max_f32_dpp instead of a copy, a move and the op).
 template <int CTRL> __device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                                                 CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]

@@ -463,7 +463,7 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
 // 2 fb + half, and mt < D/16 a value tile or mt = D/16 the z row.
 // mode 0 (bidirectional): sum over the segment partials, rescaled to the
 //   block's maximum shift; written as the packed A operand of the output
-//   contraction (kvpack[bh][mt][fb][lane], kappa order over the block's 32
+//   contraction (kvpack[bh][fb][mt][lane], kappa order over the block's 32
 //   features, this half filling slots 4 half .. 4 half + 3; mt = D/16 is the
 //   z row replicated) and mmax[bh][fb].
 // mode 1 (causal): carry[bh][s] = sum over segments s' < s, scaled to
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
         T4 packed;
 #pragma unroll
         for (int i = 0; i < 4; ++i) packed[i] = (T)acc[i];
-        T4* dst = reinterpret_cast<T4*>(kvpack + (((size_t)bh * NMT + mt) * nfb + fb) * 64 + lane) + half;
+        T4* dst = reinterpret_cast<T4*>(kvpack + (((size_t)bh * nfb + fb) * NMT + mt) * 64 + lane) + half;
         *dst = packed;
         if (threadIdx.x == 0 && half == 0) mmax[(size_t)bh * nfb + fb] = Ms;
     } else {
@@ -613,6 +613,10 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
 // shift (lane-local test; the cross-lane max only when some lane needs it),
 // exponentiate into the B operand and accumulate out^T[dims | z][T].
 // ---------------------------------------------------------------------------
+// Static LDS of the output pass (the per-block key shifts, m <= 512): the
+// launcher leaves room for it beside the dynamically sized operand stages.
+constexpr int kBidirOutStaticFloats = 512 / 32;
+
 template <typename T, int D, bool OM_LDS, bool KV_LDS, int NW, bool RELU>
 __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict__ q, const vec8<T>* __restrict__ ompack,
                                                         long long om_head_vecs, const vec8<T>* __restrict__ kvpack,
@@ -650,6 +654,13 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
     const vec8<T>* kv_src = KV_LDS ? kv_stage : kvh;
     float Mstar = kNegInf;
     for (int fb = 0; fb < nfb; ++fb) Mstar = __builtin_fmaxf(Mstar, mmax[(size_t)bh * nfb + fb]);
+    // per-block key shift relative to the largest one (<= 0; -inf for an
+    // empty block), read once per block in the loop
+    __shared__ float offs[kBidirOutStaticFloats];
+    if ((int)threadIdx.x < nfb) {
+        const float mb = mmax[(size_t)bh * nfb + threadIdx.x];
+        offs[threadIdx.x] = RELU ? 0.0f : (mb == kNegInf) ? kNegInf : mb - Mstar;
+    }
     float cq[NTT];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
@@ -676,8 +687,7 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
     // projection of one 32-feature chunk for all query tiles; the next
     // chunk's projection is issued before the current chunk's exponentials
     auto project = [&](int fb, f4 (&pp)[NTT][2]) {
-        const float mb = mmax[(size_t)bh * nfb + fb];
-        const float off = RELU ? 0.0f : (mb == kNegInf) ? kNegInf : mb - Mstar;  // per-block key shift, <= 0
+        const float off = offs[fb];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
@@ -691,27 +701,24 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
                 for (int tt = 0; tt < NTT; ++tt) pp[tt][hh] = mma32(a, xq[tt][ks], pp[tt][hh]);
             }
     };
-    f4 pn[NTT][2];
-    project(0, pn);
-    // the first chunk sets each query's shift to its maximum (ReLU: none)
+    // projections of two consecutive 32-feature blocks, used in turn (the
+    // loop body runs twice per iteration with the roles swapped: no copies)
+    f4 pa[NTT][2], pb[NTT][2];
+    project(0, pa);
+    // the first block sets each query's shift to its maximum (ReLU: none)
 #pragma unroll
     for (int tt = 0; tt < (RELU ? 0 : NTT); ++tt) {
         float lm = kNegInf;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lm = __builtin_fmaxf(lm, pn[tt][hh][i]);
+            for (int i = 0; i < 4; ++i) lm = __builtin_fmaxf(lm, pa[tt][hh][i]);
         sref[tt] = col_max(lm);
-        pn[tt][0] -= sref[tt];
-        pn[tt][1] -= sref[tt];
+        pa[tt][0] -= sref[tt];
+        pa[tt][1] -= sref[tt];
     }
-    for (int fb = 0; fb < nfb; ++fb) {
-        f4 p[NTT][2];
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            p[tt][0] = pn[tt][0];
-            p[tt][1] = pn[tt][1];
-        }
+    // block fb: its projection is in p; the next block's goes into pn
+    auto block = [&](int fb, f4 (&p)[NTT][2], f4 (&pn)[NTT][2]) {
         const bool more = fb + 1 < nfb;
         if (more) project(fb + 1, pn);
         float lm[NTT];
@@ -756,13 +763,22 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
             }
             bq[tt] = pack8t<T>(e0, e1);
         }
+        // the block's [KV | z]^T operands are contiguous (block-major layout):
+        // one address per block plus immediate offsets
+        const vec8<T>* kb = kv_src + (size_t)fb * NMT * 64 + lane;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
-            const vec8<T> a = kv_src[((size_t)mt * nfb + fb) * 64 + lane];
+            const vec8<T> a = kb[mt * 64];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) acc[mt][tt] = mma32(a, bq[tt], acc[mt][tt]);
         }
+    };
+    int fb = 0;
+    for (; fb + 1 < nfb; fb += 2) {
+        block(fb, pa, pb);
+        block(fb + 1, pb, pa);
     }
+    if (fb < nfb) block(fb, pa, pb);
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
         const int t = tbase + 16 * tt + r;
@@ -1960,12 +1976,13 @@ static hipError_t launch_all(const LaunchArgs& a) {
             constexpr int NW = decltype(nw_c)::value;
             const int tok_per_wg = NW * 16 * NTT;
             const int blocks = (a.L + tok_per_wg - 1) / tok_per_wg;
-            if (om_b + kv_b <= kMaxLds) {
+            constexpr size_t lds_free = kMaxLds - sizeof(float) * kBidirOutStaticFloats;
+            if (om_b + kv_b <= lds_free) {
                 auto kern = bidir_out_kernel<T, D, true, true, NW, RELU>;
                 (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(om_b + kv_b));
                 hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), om_b + kv_b, st, q, ompack, om_head_vecs, kvp,
                                    a.ws_mmax, out, a.H, a.L, a.m);
-            } else if (kv_b <= kMaxLds) {
+            } else if (kv_b <= lds_free) {
                 auto kern = bidir_out_kernel<T, D, false, true, NW, RELU>;
                 (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kv_b);
                 hipLaunchKernelGGL(kern, dim3(blocks, BH), dim3(64 * NW), kv_b, st, q, ompack, om_head_vecs, kvp, a.ws_mmax,

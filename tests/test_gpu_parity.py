@@ -377,3 +377,20 @@ def test_injected_key_spike(d, m, op):
     err = _rel(got, want)
     _log(f"key spike {op} d={d} m={m}", err, TOL["bf16"])
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("d,m", [(32, 512), (64, 512)])
+def test_bidir_f32_operands_at_the_lds_limit(d, m):
+    """fp32 shapes whose output-pass operands fill the 160 KB of LDS exactly
+    (projection + [KV | z] at d = 32, [KV | z] alone at d = 64): the launcher
+    keeps room for the kernel's static LDS and stages less."""
+    w = WORKLOADS["bidir_f32_tiny"].replace(d=d, m=m, omega_per_head=True)
+    H = 2
+    inp = make_inputs(w, B=1, H=H, L=300)
+    om = _omega(w, H)
+    q, k, v = _to_dev(inp, w.dtype)
+    got = favor.bidir(q, k, v, torch.from_numpy(om).to(_dev())).cpu().numpy().astype(np.float64)
+    want = native.bidir(inp.q, inp.k, inp.v, om)
+    err = _rel(got, want)
+    _log(f"bidir f32 d={d} m={m} at the LDS limit", err, TOL["f32"])
+    assert err <= TOL["f32"]
