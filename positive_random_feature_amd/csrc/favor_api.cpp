@@ -7,6 +7,8 @@
 
 #include "favor_kernels.h"
 
+#include <algorithm>
+
 namespace {
 
 using favor::kTargetWorkgroups;
@@ -67,6 +69,14 @@ Plan make_plan(int op, const favor_shape& s, int segments = 0) {
     const bool wide = op == FAVOR_OP_CAUSAL && s.dtype == FAVOR_BF16 && D == 128 && (m == 256 || m == 512);
     const int per_seg = op == FAVOR_OP_BIDIR ? BH * nfg : BH * (wide ? 2 : 1);
     int nseg = segments > 0 ? segments : (kTargetWorkgroups + per_seg - 1) / per_seg;
+    // bidirectional segments of at least 256 tokens when the partial sums are
+    // large (m >= 128): shorter ones cost more in the merge than they add in
+    // parallelism
+    if (segments <= 0 && op == FAVOR_OP_BIDIR && m >= 128) nseg = std::min(nseg, std::max(1, s.L / 256));
+    // many heads of short bidirectional sequences: one segment per head, so
+    // the call runs as one kernel (a workgroup per head does the sums and
+    // the output pass); with fewer heads the segments' parallelism wins
+    if (segments <= 0 && op == FAVOR_OP_BIDIR && s.L <= 512 && BH >= 64) nseg = 1;
     if (nseg < 1) nseg = 1;
     if (nseg > tiles) nseg = tiles;
     const int per = (s.L + nseg - 1) / nseg;

@@ -249,11 +249,14 @@ __device__ __forceinline__ size_t seg_v_off(int ft, int nt, int lane) {
 // order, transpose reads) the B operand of the update.
 // Output: partial[bh][seg][f][0..D] (column D = sum of phi), pmax[bh][seg][f/32].
 // ---------------------------------------------------------------------------
+// The sums of one (segment, head, feature group), by the eight waves of the
+// calling workgroup: the kernel below runs one per workgroup, and the
+// one-kernel bidirectional path runs it for a whole head.
 template <typename T, int D, int PD, bool RELU>
-__global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k, const T* __restrict__ v,
-                                                         const float* __restrict__ omega, int om_per_head,
-                                                         float* __restrict__ partial, float* __restrict__ pmax, int H,
-                                                         int L, int m, int seg_len, int nseg) {
+__device__ __forceinline__ void kv_partial_block(const T* __restrict__ k, const T* __restrict__ v,
+                                                 const float* __restrict__ omega, int om_per_head,
+                                                 float* __restrict__ partial, float* __restrict__ pmax, int H, int L,
+                                                 int m, int seg_len, int nseg, int seg, int bh, int fgroup) {
     using TL = LdsTile<T, D>;
     constexpr int RS = TL::RS;
     constexpr int KSD = D < 32 ? 1 : D / 32;
@@ -266,8 +269,8 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
     __shared__ float norms[3][ST];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
-    const int seg = blockIdx.x, bh = blockIdx.y, h = bh % H;
-    const int f0 = blockIdx.z * 256 + w * FW;
+    const int h = bh % H;
+    const int f0 = fgroup * 256 + w * FW;
     // The last feature group may have fewer than 8 waves' worth of features:
     // the spare waves still load tiles and meet every barrier, but compute and
     // write nothing.
@@ -457,6 +460,15 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
     if (lane == 0) pmax[((size_t)bh * nseg + seg) * (m / 32) + f0 / 32] = M;
 }
 
+template <typename T, int D, int PD, bool RELU>
+__global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                         const float* __restrict__ omega, int om_per_head,
+                                                         float* __restrict__ partial, float* __restrict__ pmax, int H,
+                                                         int L, int m, int seg_len, int nseg) {
+    kv_partial_block<T, D, PD, RELU>(k, v, omega, om_per_head, partial, pmax, H, L, m, seg_len, nseg, blockIdx.x,
+                                     blockIdx.y, blockIdx.z);
+}
+
 // ---------------------------------------------------------------------------
 // merge_scan: one workgroup per (32-feature block, head, half); thread
 // (mt, lane) owns one 4-float piece of a result tile: feature tile
@@ -617,62 +629,58 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
 // launcher leaves room for it beside the dynamically sized operand stages.
 constexpr int kBidirOutStaticFloats = 512 / 32;
 
-template <typename T, int D, bool OM_LDS, bool KV_LDS, int NW, bool RELU>
-__global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict__ q, const vec8<T>* __restrict__ ompack,
-                                                        long long om_head_vecs, const vec8<T>* __restrict__ kvpack,
-                                                        const float* __restrict__ mmax, T* __restrict__ out, int H,
-                                                        int L, int m) {
+constexpr int kOutTiles = 2;  // query tiles (16 queries each) per wave
+
+// The query operands of one wave's query tiles (rows tbase + 16 tt + r).
+// Rows past the end repeat row L - 1: the products are column-independent
+// and those columns are never stored, so the loads need no branch (a branch
+// here makes the compiler wait for them before the operand staging).
+template <typename T, int D>
+__device__ __forceinline__ void load_queries(const T* __restrict__ q, size_t xbase, int L, int tbase,
+                                             vec8<T> (&xq)[kOutTiles][D < 32 ? 1 : D / 32]) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
-    constexpr int NMT = D / 16 + 1;
-    constexpr int NTT = 2;  // query tiles per wave
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    const int nft = m / 16, nfb = m / 32;
-    vec8<T>* kv_stage = reinterpret_cast<vec8<T>*>(smem_raw);
-    vec8<T>* om_stage = kv_stage + (KV_LDS ? (size_t)NMT * nfb * 64 : 0);
-
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
-    const int bh = blockIdx.y, h = bh % H;
-    const int tbase = (blockIdx.x * (blockDim.x >> 6) + w) * (16 * NTT);
-    const size_t xbase = (size_t)bh * L * D;
-
-    // query operands first, so their latency overlaps the staging below
-    vec8<T> xq[NTT][KSD];
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-        const int t = tbase + 16 * tt + r;
+    for (int tt = 0; tt < kOutTiles; ++tt) {
+        const int t = min(tbase + 16 * tt + r, L - 1);
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
-            const bool in = t < L && (D >= 32 || g < D / 8);
-            xq[tt][ks] = in ? load8(q + xbase + (size_t)t * D + 32 * ks + 8 * g) : zero8<T>();
+            if (D >= 32)
+                xq[tt][ks] = load8(q + xbase + (size_t)t * D + 32 * ks + 8 * g);
+            else  // d = 16: lanes g >= 2 hold the zero padding of the contraction
+                xq[tt][ks] = g < D / 8 ? load8(q + xbase + (size_t)t * D + 8 * g) : zero8<T>();
         }
     }
-    const vec8<T>* omh = ompack + (size_t)(om_head_vecs ? h : 0) * (size_t)om_head_vecs;
-    const vec8<T>* kvh = kvpack + (size_t)bh * NMT * nfb * 64;
-    if (OM_LDS) copy_to_lds_async<64 * NW>(om_stage, omh, nft * KSD * 64);
-    if (KV_LDS) copy_to_lds_async<64 * NW>(kv_stage, kvh, NMT * nfb * 64);
-    const vec8<T>* om_src = OM_LDS ? om_stage : omh;
-    const vec8<T>* kv_src = KV_LDS ? kv_stage : kvh;
-    float Mstar = kNegInf;
-    for (int fb = 0; fb < nfb; ++fb) Mstar = __builtin_fmaxf(Mstar, mmax[(size_t)bh * nfb + fb]);
-    // per-block key shift relative to the largest one (<= 0; -inf for an
-    // empty block), read once per block in the loop
-    __shared__ float offs[kBidirOutStaticFloats];
-    if ((int)threadIdx.x < nfb) {
-        const float mb = mmax[(size_t)bh * nfb + threadIdx.x];
-        offs[threadIdx.x] = RELU ? 0.0f : (mb == kNegInf) ? kNegInf : mb - Mstar;
-    }
-    float cq[NTT];
+}
+
+// Their row constants -log2(e) |q|^2 / 2 (0 for ReLU features); computed
+// after the operand staging is issued, so its latency overlaps the loads.
+template <typename T, int D, bool RELU>
+__device__ __forceinline__ void query_consts(const vec8<T> (&xq)[kOutTiles][D < 32 ? 1 : D / 32],
+                                             float (&cq)[kOutTiles]) {
+    constexpr int KSD = D < 32 ? 1 : D / 32;
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
+    for (int tt = 0; tt < kOutTiles; ++tt) {
         float ss = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) ss += sumsq8(xq[tt][ks]);
         cq[tt] = RELU ? 0.0f : -0.5f * kLog2e * col_sum(ss);
     }
-    lds_dma_wait();
-    __syncthreads();
-    if (tbase >= L) return;
+}
 
+// The output pass over one wave's query tiles, from the packed projection
+// operands (om_src), the block-major [KV | z]^T operand (kv_src) and the
+// per-block key shifts (offs, relative to the largest): loops over the m/32
+// feature blocks and writes the normalised outputs.
+template <typename T, int D, bool RELU>
+__device__ __forceinline__ void out_tiles(const vec8<T>* om_src, const vec8<T>* kv_src, const float* offs,
+                                          const vec8<T> (&xq)[kOutTiles][D < 32 ? 1 : D / 32],
+                                          const float (&cq)[kOutTiles], T* __restrict__ out, size_t xbase, int L,
+                                          int nfb, int tbase) {
+    constexpr int KSD = D < 32 ? 1 : D / 32;
+    constexpr int NMT = D / 16 + 1;
+    constexpr int NTT = kOutTiles;
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     f4 acc[NMT][NTT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
@@ -786,6 +794,121 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
         const float inv = 1.0f / acc[NMT - 1][tt][0];
 #pragma unroll
         for (int mt = 0; mt < NMT - 1; ++mt) store4(out + xbase + (size_t)t * D + 16 * mt + 4 * g, acc[mt][tt] * inv);
+    }
+}
+
+
+template <typename T, int D, bool OM_LDS, bool KV_LDS, int NW, bool RELU>
+__global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict__ q, const vec8<T>* __restrict__ ompack,
+                                                        long long om_head_vecs, const vec8<T>* __restrict__ kvpack,
+                                                        const float* __restrict__ mmax, T* __restrict__ out, int H,
+                                                        int L, int m) {
+    constexpr int KSD = D < 32 ? 1 : D / 32;
+    constexpr int NMT = D / 16 + 1;
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    const int nft = m / 16, nfb = m / 32;
+    vec8<T>* kv_stage = reinterpret_cast<vec8<T>*>(smem_raw);
+    vec8<T>* om_stage = kv_stage + (KV_LDS ? (size_t)NMT * nfb * 64 : 0);
+
+    const int w = threadIdx.x >> 6;
+    const int bh = blockIdx.y, h = bh % H;
+    const int tbase = (blockIdx.x * (blockDim.x >> 6) + w) * (16 * kOutTiles);
+    const size_t xbase = (size_t)bh * L * D;
+
+    // query operands first, so their latency overlaps the staging below
+    vec8<T> xq[kOutTiles][KSD];
+    load_queries<T, D>(q, xbase, L, tbase, xq);
+    const vec8<T>* omh = ompack + (size_t)(om_head_vecs ? h : 0) * (size_t)om_head_vecs;
+    const vec8<T>* kvh = kvpack + (size_t)bh * NMT * nfb * 64;
+    if (OM_LDS) copy_to_lds_async<64 * NW>(om_stage, omh, nft * KSD * 64);
+    if (KV_LDS) copy_to_lds_async<64 * NW>(kv_stage, kvh, NMT * nfb * 64);
+    const vec8<T>* om_src = OM_LDS ? om_stage : omh;
+    const vec8<T>* kv_src = KV_LDS ? kv_stage : kvh;
+    float Mstar = kNegInf;
+    for (int fb = 0; fb < nfb; ++fb) Mstar = __builtin_fmaxf(Mstar, mmax[(size_t)bh * nfb + fb]);
+    // per-block key shift relative to the largest one (<= 0; -inf for an
+    // empty block), read once per block in the loop
+    __shared__ float offs[kBidirOutStaticFloats];
+    if ((int)threadIdx.x < nfb) {
+        const float mb = mmax[(size_t)bh * nfb + threadIdx.x];
+        offs[threadIdx.x] = RELU ? 0.0f : (mb == kNegInf) ? kNegInf : mb - Mstar;
+    }
+    float cq[kOutTiles];
+    query_consts<T, D, RELU>(xq, cq);
+    lds_dma_wait();
+    __syncthreads();
+    if (tbase >= L) return;
+    out_tiles<T, D, RELU>(om_src, kv_src, offs, xq, cq, out, xbase, L, nfb, tbase);
+}
+
+// ---------------------------------------------------------------------------
+// bidir_head: the whole bidirectional operation of one head in one workgroup
+// of eight waves, for plans that give each head a single segment (short
+// sequences, or enough heads to fill the chip; m <= 256): the head's sums
+// over the whole sequence (kv_partial_block), then the output operands built
+// straight into LDS (with one segment the merge is a conversion: the packed
+// projection from fp32, [KV | z]^T block-major from the sums, the per-block
+// shifts), then the output pass, each wave taking query tiles in turn.  One
+// launch instead of three; the results equal those of the three kernels on
+// the same one-segment plan.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int PD, bool RELU>
+__global__ __launch_bounds__(512) void bidir_head_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                         const T* __restrict__ v, const float* __restrict__ omega,
+                                                         int om_per_head, float* __restrict__ partial,
+                                                         float* __restrict__ pmax, T* __restrict__ out, int H, int L,
+                                                         int m) {
+    constexpr int KSD = D < 32 ? 1 : D / 32;
+    constexpr int NTV = D / 16;
+    constexpr int NMT = NTV + 1;
+    typedef __attribute__((ext_vector_type(4))) T T4;
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    const int nft = m / 16, nfb = m / 32;
+    vec8<T>* kv_stage = reinterpret_cast<vec8<T>*>(smem_raw);
+    vec8<T>* om_stage = kv_stage + (size_t)NMT * nfb * 64;
+    const int bh = blockIdx.x, h = bh % H;
+
+    kv_partial_block<T, D, PD, RELU>(k, v, omega, om_per_head, partial, pmax, H, L, m, L, 1, 0, bh, 0);
+    __syncthreads();  // this workgroup's sums and shifts are written
+
+    // [KV | z]^T operand, block-major (fb, mt, lane), each lane slot holding
+    // the two 16-feature halves of block fb (the layout the merge pass writes)
+    const float* ps = partial + (size_t)bh * m * (D + 1);
+    for (int e = threadIdx.x; e < nfb * NMT * 64 * 2; e += blockDim.x) {
+        const int half = e & 1, lane = (e >> 1) & 63, mt = (e >> 7) % NMT, fb = (e >> 7) / NMT;
+        const int ft = 2 * fb + half;
+        const size_t o = mt < NTV ? seg_v_off<D>(ft, mt, lane) : (size_t)m * D + 16 * ft + 4 * (lane >> 4);
+        const f4 x = *reinterpret_cast<const f4*>(ps + o);
+        T4 pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = (T)x[i];
+        reinterpret_cast<T4*>(kv_stage + ((size_t)fb * NMT + mt) * 64 + lane)[half] = pk;
+    }
+    // projection operands, packed from fp32 (the order the merge pass packs)
+    const float* omh = omega + (om_per_head ? (size_t)h * m * D : 0);
+    for (int e = threadIdx.x; e < nft * KSD * 64; e += blockDim.x) {
+        const int ln = e & 63, ks = (e >> 6) % KSD, ft = (e >> 6) / KSD;
+        om_stage[e] = omega_operand<T, D>(omh, 16 * ft + (ln & 15), ks, ln >> 4);
+    }
+    // per-block key shifts relative to the largest
+    __shared__ float offs[kBidirOutStaticFloats];
+    if ((int)threadIdx.x < nfb) {
+        const float* pm = pmax + (size_t)bh * nfb;
+        float Mstar = kNegInf;
+        for (int fb = 0; fb < nfb; ++fb) Mstar = __builtin_fmaxf(Mstar, pm[fb]);
+        const float mb = pm[threadIdx.x];
+        offs[threadIdx.x] = RELU ? 0.0f : (mb == kNegInf) ? kNegInf : mb - Mstar;
+    }
+    __syncthreads();
+
+    const size_t xbase = (size_t)bh * L * D;
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int tbase = w * 16 * kOutTiles; tbase < L; tbase += nw * 16 * kOutTiles) {
+        vec8<T> xq[kOutTiles][KSD];
+        float cq[kOutTiles];
+        load_queries<T, D>(q, xbase, L, tbase, xq);
+        query_consts<T, D, RELU>(xq, cq);
+        out_tiles<T, D, RELU>(om_stage, kv_stage, offs, xq, cq, out, xbase, L, nfb, tbase);
     }
 }
 
@@ -1957,6 +2080,25 @@ static hipError_t launch_all(const LaunchArgs& a) {
     const int nfg = (a.m + 255) / 256;
     stage_event(a, 0);
     constexpr int PD_KV = D >= 128 ? 1 : 2;
+    // one segment per head: the one-kernel bidirectional path when its
+    // operand stages fit beside the sums' static LDS
+    if (a.op == OpKind::Bidir && a.nseg == 1 && a.m <= 256) {
+        auto kern = bidir_head_kernel<T, D, PD_KV, RELU>;
+        static const size_t static_lds = [kern] {
+            hipFuncAttributes at{};
+            return hipFuncGetAttributes(&at, (const void*)kern) == hipSuccess ? (size_t)at.sharedSizeBytes
+                                                                              : kMaxLds;
+        }();
+        constexpr int KSD = D < 32 ? 1 : D / 32;
+        const size_t dyn = sizeof(vec8<T>) * 64 * ((size_t)(D / 16 + 1) * (a.m / 32) + (size_t)(a.m / 16) * KSD);
+        if (static_lds + dyn <= kMaxLds) {
+            (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+            hipLaunchKernelGGL(kern, dim3(BH), dim3(512), dyn, st, q, k, v, a.omega, per_head, a.ws_partial, a.ws_pmax,
+                               out, a.H, a.L, a.m);
+            for (int i = 1; i <= 3; ++i) stage_event(a, i);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((kv_partial_kernel<T, D, PD_KV, RELU>), dim3(a.nseg, BH, nfg), dim3(512), 0, st, k, v, a.omega, per_head,
                        a.ws_partial, a.ws_pmax, a.H, a.L, a.m, a.seg_len, a.nseg);
     stage_event(a, 1);
