@@ -85,13 +85,14 @@ Plan make_plan(int op, const favor_shape& s, int segments = 0) {
     p.seg_len = ((per + gran - 1) / gran) * gran;
     p.nseg = (s.L + p.seg_len - 1) / p.seg_len;
     const size_t rows = (size_t)BH * p.nseg * m;
-    p.partial = align256(rows * (D + 1) * sizeof(float));
+    // segment sums in the input type (bf16 sums feed bf16 operands downstream)
+    p.partial = align256(rows * (D + 1) * (s.dtype == FAVOR_BF16 ? 2 : sizeof(float)));
     p.pmax = align256((size_t)BH * p.nseg * (m / 32) * sizeof(float));
     if (op == FAVOR_OP_BIDIR) {
         p.kvpack = align256((size_t)BH * (D / 16 + 1) * (m / 32) * 64 * vec8);
         p.mmax = align256((size_t)BH * (m / 32) * sizeof(float));
     } else {
-        p.carry = align256(rows * (D + 1) * sizeof(float));
+        p.carry = align256(rows * (D + 1) * (s.dtype == FAVOR_BF16 ? 2 : sizeof(float)));
         p.cmax = align256((size_t)BH * p.nseg * (m / 32) * sizeof(float));
     }
     p.total = p.ompack + p.partial + p.pmax + p.kvpack + p.mmax + p.carry + p.cmax;
@@ -210,11 +211,11 @@ favor_status run(const Call& c) {
     char* base = static_cast<char*>(c.ws);
     size_t off = 0;
     a.ws_ompack = base + off; off += p.ompack;
-    a.ws_partial = reinterpret_cast<float*>(base + off); off += p.partial;
+    a.ws_partial = base + off; off += p.partial;
     a.ws_pmax = reinterpret_cast<float*>(base + off); off += p.pmax;
     a.ws_kvpack = base + off; off += p.kvpack;
     a.ws_mmax = reinterpret_cast<float*>(base + off); off += p.mmax;
-    a.ws_carry = reinterpret_cast<float*>(base + off); off += p.carry;
+    a.ws_carry = base + off; off += p.carry;
     a.ws_cmax = reinterpret_cast<float*>(base + off); off += p.cmax;
     a.state_in = c.state_in;
     a.state_out = c.state_out;

@@ -274,4 +274,11 @@ __device__ __forceinline__ void store4(bf16* p, f4 v) {
 }
 __device__ __forceinline__ void store4(float* p, f4 v) { *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]}; }
 
+// Load 4 consecutive elements as fp32.
+__device__ __forceinline__ f4 load4f(const bf16* p) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+    return f4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+__device__ __forceinline__ f4 load4f(const float* p) { return *reinterpret_cast<const f4*>(p); }
+
 }  // namespace favor

@@ -32,11 +32,11 @@ struct LaunchArgs {
     int chunk;          // causal: tokens per scan step (32 or 64)
     // workspace regions
     void* ws_ompack;
-    float* ws_partial;
+    void* ws_partial;  // segment sums, in the input type
     float* ws_pmax;
     void* ws_kvpack;
     float* ws_mmax;
-    float* ws_carry;
+    void* ws_carry;  // causal carries, in the input type
     float* ws_cmax;
     // causal only: carried-in and carried-out prefix state (nullptr: none);
     // per head m (d + 1) + 1 floats, see favor_causal_state

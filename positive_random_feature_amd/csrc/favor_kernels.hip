@@ -225,10 +225,14 @@ __device__ __forceinline__ vec8<T> omega_operand(const float* om_head, int f, in
 
 // ---------------------------------------------------------------------------
 // Segment sums (partials, causal carries) of one (head, segment) in the
-// matrix-core result layout, so that every lane moves 16 aligned bytes:
+// matrix-core result layout, so that every lane moves 4 consecutive
+// elements (aligned):
 //   V part: ((ft * D/16 + nt) * 64 + lane) * 4 + i holds S[16 ft + 4 g + i][16 nt + r]
 //   z part: m * D + f holds S[f][D] (the sum of phi)
-// m (D + 1) floats in all.
+// m (D + 1) elements in all, stored in the input type: fp32 for fp32 inputs;
+// bf16 for bf16 inputs, whose downstream operands (the output contraction's
+// [KV | z], the scan's state products) are rounded to bf16 anyway.  The sums
+// are accumulated in fp32 and rounded once when stored.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ size_t seg_v_off(int ft, int nt, int lane) {
@@ -247,7 +251,8 @@ __device__ __forceinline__ size_t seg_v_off(int ft, int nt, int lane) {
 // lane-local test; the wave-wide max only when some value exceeds kTau), with
 // exact rescaling of the sums.  phi is the A operand and [V | 1] (kappa
 // order, transpose reads) the B operand of the update.
-// Output: partial[bh][seg][f][0..D] (column D = sum of phi), pmax[bh][seg][f/32].
+// Output: partial[bh][seg][f][0..D] (column D = sum of phi; input type),
+// pmax[bh][seg][f/32].
 // ---------------------------------------------------------------------------
 // The sums of one (segment, head, feature group), by the eight waves of the
 // calling workgroup: the kernel below runs one per workgroup, and the
@@ -255,7 +260,7 @@ __device__ __forceinline__ size_t seg_v_off(int ft, int nt, int lane) {
 template <typename T, int D, int PD, bool RELU>
 __device__ __forceinline__ void kv_partial_block(const T* __restrict__ k, const T* __restrict__ v,
                                                  const float* __restrict__ omega, int om_per_head,
-                                                 float* __restrict__ partial, float* __restrict__ pmax, int H, int L,
+                                                 T* __restrict__ partial, float* __restrict__ pmax, int H, int L,
                                                  int m, int seg_len, int nseg, int seg, int bh, int fgroup) {
     using TL = LdsTile<T, D>;
     constexpr int RS = TL::RS;
@@ -449,13 +454,13 @@ __device__ __forceinline__ void kv_partial_block(const T* __restrict__ k, const 
     }
 
     if (!active) return;
-    float* pp = partial + ((size_t)bh * nseg + seg) * (size_t)m * (D + 1);
+    T* pp = partial + ((size_t)bh * nseg + seg) * (size_t)m * (D + 1);
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft) {
         const int fg = f0 / 16 + ft;
 #pragma unroll
-        for (int nt = 0; nt < NT - 1; ++nt) *reinterpret_cast<f4*>(pp + seg_v_off<D>(fg, nt, lane)) = kv[ft][nt];
-        if (r == 0) *reinterpret_cast<f4*>(pp + (size_t)m * D + 16 * fg + 4 * g) = kv[ft][NT - 1];
+        for (int nt = 0; nt < NT - 1; ++nt) store4(pp + seg_v_off<D>(fg, nt, lane), kv[ft][nt]);
+        if (r == 0) store4(pp + (size_t)m * D + 16 * fg + 4 * g, kv[ft][NT - 1]);
     }
     if (lane == 0) pmax[((size_t)bh * nseg + seg) * (m / 32) + f0 / 32] = M;
 }
@@ -463,7 +468,7 @@ __device__ __forceinline__ void kv_partial_block(const T* __restrict__ k, const 
 template <typename T, int D, int PD, bool RELU>
 __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                          const float* __restrict__ omega, int om_per_head,
-                                                         float* __restrict__ partial, float* __restrict__ pmax, int H,
+                                                         T* __restrict__ partial, float* __restrict__ pmax, int H,
                                                          int L, int m, int seg_len, int nseg) {
     kv_partial_block<T, D, PD, RELU>(k, v, omega, om_per_head, partial, pmax, H, L, m, seg_len, nseg, blockIdx.x,
                                      blockIdx.y, blockIdx.z);
@@ -480,7 +485,8 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
 //   z row replicated) and mmax[bh][fb].
 // mode 1 (causal): carry[bh][s] = sum over segments s' < s, scaled to
 //   cmax[bh][s][fb] = max over s' <= s of the partial shifts (every key of
-//   segment s has exponents <= cmax + kTau), in the segment-sum layout.
+//   segment s has exponents <= cmax + kTau), in the segment-sum layout and
+//   type (summed in fp32).
 //   A carried-in state (state_in, per head: G[m][D] row-major, z[m], and a
 //   natural-log shift s, true values = stored * e^s) enters as a segment
 //   before the first, with shift s log2(e) in every block; state_out
@@ -491,9 +497,9 @@ __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
-    const float* __restrict__ partial, const float* __restrict__ pmax, const float* __restrict__ omega, int om_per_head,
+    const T* __restrict__ partial, const float* __restrict__ pmax, const float* __restrict__ omega, int om_per_head,
     int H, int m, int nseg, int mode, vec8<T>* __restrict__ kvpack, float* __restrict__ mmax,
-    float* __restrict__ carry, float* __restrict__ cmax, vec8<T>* __restrict__ ompack,
+    T* __restrict__ carry, float* __restrict__ cmax, vec8<T>* __restrict__ ompack,
     const float* __restrict__ state_in, float* __restrict__ state_out) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
     constexpr int NTV = D / 16;
@@ -503,7 +509,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
     const int nfb = m / 32;
     const int mt = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
     const size_t seg_stride = (size_t)m * (D + 1);
-    const float* pb = partial + (size_t)bh * nseg * seg_stride;
+    const T* pb = partial + (size_t)bh * nseg * seg_stride;
     const float* pm = pmax + (size_t)bh * nseg * nfb;
 
     if (b == 0 && (om_per_head || h == 0)) {
@@ -534,7 +540,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
             f4 x[NB];
 #pragma unroll
             for (int j = 0; j < NB; ++j)  // independent loads in flight
-                x[j] = *reinterpret_cast<const f4*>(pb + (size_t)min(s0 + j, nseg - 1) * seg_stride + o);
+                x[j] = load4f(pb + (size_t)min(s0 + j, nseg - 1) * seg_stride + o);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const float ms = s0 + j < nseg ? pms[s0 + j] : kNegInf;
@@ -549,7 +555,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
         *dst = packed;
         if (threadIdx.x == 0 && half == 0) mmax[(size_t)bh * nfb + fb] = Ms;
     } else {
-        float* cb = carry + (size_t)bh * nseg * seg_stride;
+        T* cb = carry + (size_t)bh * nseg * seg_stride;
         const bool writer = mt < NTV || r == 0;  // the z row: one lane per 4 features
         const size_t st_stride = (size_t)m * (D + 1) + 1;
         // this thread's piece in the row-major state: features 16 ft + 4 g + i,
@@ -572,7 +578,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
             f4 x[NB];
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                x[j] = *reinterpret_cast<const f4*>(pb + (size_t)min(s0 + j, nseg - 1) * seg_stride + o);
+                x[j] = load4f(pb + (size_t)min(s0 + j, nseg - 1) * seg_stride + o);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int s = s0 + j;
@@ -582,7 +588,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 1)) void merge_scan_kernel(
                         acc *= (Mrun == kNegInf ? 0.0f : exp2f_fast(Mrun - ms));
                         Mrun = ms;
                     }
-                    if (writer) *reinterpret_cast<f4*>(cb + (size_t)s * seg_stride + o) = acc;
+                    if (writer) store4(cb + (size_t)s * seg_stride + o, acc);
                     if (ms != kNegInf) acc += exp2f_fast(ms - Mrun) * x[j];
                 }
             }
@@ -855,7 +861,7 @@ __global__ __launch_bounds__(64 * NW) void bidir_out_kernel(const T* __restrict_
 template <typename T, int D, int PD, bool RELU>
 __global__ __launch_bounds__(512) void bidir_head_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                          const T* __restrict__ v, const float* __restrict__ omega,
-                                                         int om_per_head, float* __restrict__ partial,
+                                                         int om_per_head, T* __restrict__ partial,
                                                          float* __restrict__ pmax, T* __restrict__ out, int H, int L,
                                                          int m) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
@@ -873,12 +879,12 @@ __global__ __launch_bounds__(512) void bidir_head_kernel(const T* __restrict__ q
 
     // [KV | z]^T operand, block-major (fb, mt, lane), each lane slot holding
     // the two 16-feature halves of block fb (the layout the merge pass writes)
-    const float* ps = partial + (size_t)bh * m * (D + 1);
+    const T* ps = partial + (size_t)bh * m * (D + 1);
     for (int e = threadIdx.x; e < nfb * NMT * 64 * 2; e += blockDim.x) {
         const int half = e & 1, lane = (e >> 1) & 63, mt = (e >> 7) % NMT, fb = (e >> 7) / NMT;
         const int ft = 2 * fb + half;
         const size_t o = mt < NTV ? seg_v_off<D>(ft, mt, lane) : (size_t)m * D + 16 * ft + 4 * (lane >> 4);
-        const f4 x = *reinterpret_cast<const f4*>(ps + o);
+        const f4 x = load4f(ps + o);
         T4 pk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) pk[i] = (T)x[i];
@@ -978,7 +984,7 @@ __device__ __forceinline__ void causal_reduce(const float* part, const float* pl
 template <typename T, int D, int FW, int W, int PARTS, int PD, bool OM_REGS, bool RELU>
 __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                               const T* __restrict__ v, const vec8<T>* __restrict__ ompack,
-                                                              long long om_head_vecs, const float* __restrict__ carry,
+                                                              long long om_head_vecs, const T* __restrict__ carry,
                                                               const float* __restrict__ cmax, T* __restrict__ out, int H,
                                                               int L, int m, int seg_len, int nseg) {
     using TL = LdsTile<T, D>;
@@ -1029,7 +1035,7 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
     for (int b = 0; b < KSF; ++b) M = __builtin_fmaxf(M, cm[f0 / 32 + b]);
     f4 G[NFT][NT];
     {
-        const float* cb = carry + ((size_t)bh * nseg + seg) * (size_t)m * D1;
+        const T* cb = carry + ((size_t)bh * nseg + seg) * (size_t)m * D1;
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft) {
             const float mb = cm[(f0 + 16 * ft) / 32];
@@ -1038,7 +1044,7 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const size_t o = nt < NT - 1 ? seg_v_off<D>(fg, nt, lane) : (size_t)m * D + 16 * fg + 4 * g;
-                G[ft][nt] = sc * *reinterpret_cast<const f4*>(cb + o);
+                G[ft][nt] = sc * load4f(cb + o);
             }
         }
     }
@@ -1242,7 +1248,7 @@ struct TileSmem {
 template <int M, bool RELU>
 __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, const bf16x8* __restrict__ ompack,
-                                                          long long om_head_vecs, const float* __restrict__ carry,
+                                                          long long om_head_vecs, const bf16* __restrict__ carry,
                                                           const float* __restrict__ cmax, bf16* __restrict__ out, int H,
                                                           int L, int seg_len, int nseg) {
     using SM = TileSmem<M>;
@@ -1299,12 +1305,12 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
     f4 G[NFT];
     f4 Z[2 * ZB];
     if (!qwave) {
-        const float* cb = carry + ((size_t)bh * nseg + seg) * (size_t)M * D1;
+        const bf16* cb = carry + ((size_t)bh * nseg + seg) * (size_t)M * D1;
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft) {
             const float mb = cm[ft / 2];
             const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
-            G[ft] = sc * *reinterpret_cast<const f4*>(cb + seg_v_off<D>(ft, s, lane));
+            G[ft] = sc * load4f(cb + seg_v_off<D>(ft, s, lane));
         }
 #pragma unroll
         for (int zb = 0; zb < ZB; ++zb) {
@@ -1314,7 +1320,7 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
             const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
-                Z[2 * zb + hf] = own ? sc * *reinterpret_cast<const f4*>(cb + (size_t)M * D + 32 * kb + 16 * hf + 4 * g)
+                Z[2 * zb + hf] = own ? sc * load4f(cb + (size_t)M * D + 32 * kb + 16 * hf + 4 * g)
                                      : f4splat(0.0f);
         }
     }
@@ -1666,7 +1672,7 @@ struct WideSmem {
 template <int M, bool RELU>
 __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, const bf16x8* __restrict__ ompack,
-                                                          long long om_head_vecs, const float* __restrict__ carry,
+                                                          long long om_head_vecs, const bf16* __restrict__ carry,
                                                           const float* __restrict__ cmax, bf16* __restrict__ out, int H,
                                                           int L, int seg_len, int nseg) {
     using SM = WideSmem<M>;
@@ -1723,20 +1729,20 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
     f4 G[GFT];
     f4 Z[PFT];
     {
-        const float* cb = carry + ((size_t)bh * nseg + seg) * (size_t)M * D1;
+        const bf16* cb = carry + ((size_t)bh * nseg + seg) * (size_t)M * D1;
 #pragma unroll
         for (int i = 0; i < GFT; ++i) {
             const int ft = GFT * fh + i;
             const float mb = cm[ft / 2];
             const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
-            G[i] = sc * *reinterpret_cast<const f4*>(cb + seg_v_off<D>(ft, nt, lane));
+            G[i] = sc * load4f(cb + seg_v_off<D>(ft, nt, lane));
         }
 #pragma unroll
         for (int f = 0; f < PFT; ++f) {
             const int ft = PFT * w + f;
             const float mb = cm[ft / 2];
             const float sc = (mb == kNegInf) ? 0.0f : exp2f_fast(mb - Mseg);
-            Z[f] = sc * *reinterpret_cast<const f4*>(cb + (size_t)M * D + 16 * ft + 4 * g);
+            Z[f] = sc * load4f(cb + (size_t)M * D + 16 * ft + 4 * g);
         }
     }
 
@@ -2016,16 +2022,16 @@ static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long
     if constexpr (two <= kMaxLds) {
         auto kern = causal_chunk_kernel<T, D, FW, W, 2, PD, OM_REGS, RELU>;
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)two);
-        hipLaunchKernelGGL(kern, grid, block, two, a.stream, q, k, v, ompack, om_head_vecs, a.ws_carry, a.ws_cmax, out,
-                           a.H, a.L, a.m, a.seg_len, a.nseg);
+        hipLaunchKernelGGL(kern, grid, block, two, a.stream, q, k, v, ompack, om_head_vecs,
+                           static_cast<const T*>(a.ws_carry), a.ws_cmax, out, a.H, a.L, a.m, a.seg_len, a.nseg);
     } else if constexpr (CausalSmem<T, D, FW, W, 1>::BYTES > kMaxLds) {
         return hipErrorInvalidValue;  // rejected by argument validation before any launch
     } else {
         constexpr size_t one = CausalSmem<T, D, FW, W, 1>::BYTES;
         auto kern = causal_chunk_kernel<T, D, FW, W, 1, PD, OM_REGS, RELU>;
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)one);
-        hipLaunchKernelGGL(kern, grid, block, one, a.stream, q, k, v, ompack, om_head_vecs, a.ws_carry, a.ws_cmax, out,
-                           a.H, a.L, a.m, a.seg_len, a.nseg);
+        hipLaunchKernelGGL(kern, grid, block, one, a.stream, q, k, v, ompack, om_head_vecs,
+                           static_cast<const T*>(a.ws_carry), a.ws_cmax, out, a.H, a.L, a.m, a.seg_len, a.nseg);
     }
     return hipGetLastError();
 }
@@ -2038,7 +2044,7 @@ static hipError_t launch_causal_tile(const LaunchArgs& a, const bf16x8* ompack, 
     auto kern = causal_tile_kernel<M, RELU>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H), dim3(512), bytes, a.stream, q, k, v, ompack, om_head_vecs,
-                       a.ws_carry, a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
+                       static_cast<const bf16*>(a.ws_carry), a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
     return hipGetLastError();
 }
 
@@ -2050,7 +2056,7 @@ static hipError_t launch_causal_wide(const LaunchArgs& a, const bf16x8* ompack, 
     auto kern = causal_wide_kernel<M, RELU>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H, 2), dim3(512), bytes, a.stream, q, k, v, ompack, om_head_vecs,
-                       a.ws_carry, a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
+                       static_cast<const bf16*>(a.ws_carry), a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
     return hipGetLastError();
 }
 
@@ -2093,20 +2099,21 @@ static hipError_t launch_all(const LaunchArgs& a) {
         const size_t dyn = sizeof(vec8<T>) * 64 * ((size_t)(D / 16 + 1) * (a.m / 32) + (size_t)(a.m / 16) * KSD);
         if (static_lds + dyn <= kMaxLds) {
             (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-            hipLaunchKernelGGL(kern, dim3(BH), dim3(512), dyn, st, q, k, v, a.omega, per_head, a.ws_partial, a.ws_pmax,
-                               out, a.H, a.L, a.m);
+            hipLaunchKernelGGL(kern, dim3(BH), dim3(512), dyn, st, q, k, v, a.omega, per_head,
+                               reinterpret_cast<T*>(a.ws_partial), a.ws_pmax, out, a.H, a.L, a.m);
             for (int i = 1; i <= 3; ++i) stage_event(a, i);
             return hipGetLastError();
         }
     }
     hipLaunchKernelGGL((kv_partial_kernel<T, D, PD_KV, RELU>), dim3(a.nseg, BH, nfg), dim3(512), 0, st, k, v, a.omega, per_head,
-                       a.ws_partial, a.ws_pmax, a.H, a.L, a.m, a.seg_len, a.nseg);
+                       reinterpret_cast<T*>(a.ws_partial), a.ws_pmax, a.H, a.L, a.m, a.seg_len, a.nseg);
     stage_event(a, 1);
     const int nfb = a.m / 32;
     const int mode = a.op == OpKind::Bidir ? 0 : 1;
-    hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(nfb, BH, 2), dim3(64 * (D / 16 + 1)), 0, st, a.ws_partial, a.ws_pmax,
+    hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(nfb, BH, 2), dim3(64 * (D / 16 + 1)), 0, st,
+                       reinterpret_cast<const T*>(a.ws_partial), a.ws_pmax,
                        a.omega, per_head, a.H, a.m, a.nseg, mode, reinterpret_cast<vec8<T>*>(a.ws_kvpack), a.ws_mmax,
-                       a.ws_carry, a.ws_cmax, ompack, mode == 1 ? a.state_in : nullptr,
+                       static_cast<T*>(a.ws_carry), a.ws_cmax, ompack, mode == 1 ? a.state_in : nullptr,
                        mode == 1 ? a.state_out : nullptr);
     stage_event(a, 2);
     if (a.op == OpKind::Bidir) {

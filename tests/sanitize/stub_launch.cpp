@@ -48,14 +48,14 @@ hipError_t launch(const LaunchArgs& a) {
     if ((size_t)(a.nseg - 1) * a.seg_len >= (size_t)a.L) fail("an empty segment");
     if (a.nseg > kMaxSeg) fail("more segments than the merge pass holds");
     const size_t rows = BH * a.nseg * a.m;
-    region(a.ws_partial, rows * (a.D + 1) * sizeof(float), "partial");
+    region(a.ws_partial, rows * (a.D + 1) * eb, "partial");  // segment sums in the input type
     region(a.ws_pmax, BH * a.nseg * (a.m / 32) * sizeof(float), "pmax");
     if (a.op == OpKind::Bidir) {
         region(a.ws_kvpack, BH * (a.D / 16 + 1) * (a.m / 32) * 64 * 8 * eb, "kvpack");
         region(a.ws_mmax, BH * (a.m / 32) * sizeof(float), "mmax");
     } else {
         if (a.chunk != 32 && a.chunk != 64) fail("bad chunk");
-        region(a.ws_carry, rows * (a.D + 1) * sizeof(float), "carry");
+        region(a.ws_carry, rows * (a.D + 1) * eb, "carry");  // in the input type
         region(a.ws_cmax, BH * a.nseg * (a.m / 32) * sizeof(float), "cmax");
     }
     return hipSuccess;

@@ -298,7 +298,7 @@ def test_noalloc_validation(lib):
     assert f(ctypes.byref(shp(B=0)), P_Q, P_K, P_V, P_OM, P_O, 0, None) == INVALID
     assert f(ctypes.byref(shp(d=48)), P_Q, P_K, P_V, P_OM, P_O, 0, None) == UNSUPPORTED
     assert f(ctypes.byref(shp()), P_Q, P_K, P_V, P_OM, P_O, 16, None) == UNSUPPORTED
-    big = shp(B=1, H=256, L=128, d=128, m=512)
+    big = shp(B=1, H=512, L=128, d=128, m=512)
     assert lib.favor_workspace_bytes(2, ctypes.byref(big), 0) > _lib.FAVOR_NOALLOC_SCRATCH_BYTES
     assert f(ctypes.byref(big), P_Q, P_K, P_V, P_OM, P_O, 0, None) == WORKSPACE
     # the benchmarked causal workloads fit
