@@ -75,8 +75,13 @@ Plan make_plan(int op, const favor_shape& s, int segments = 0) {
     if (segments <= 0 && op == FAVOR_OP_BIDIR && m >= 128) nseg = std::min(nseg, std::max(1, s.L / 256));
     // many heads of short bidirectional sequences: one segment per head, so
     // the call runs as one kernel (a workgroup per head does the sums and
-    // the output pass); with fewer heads the segments' parallelism wins
-    if (segments <= 0 && op == FAVOR_OP_BIDIR && s.L <= 512 && BH >= 64) nseg = 1;
+    // the output pass) where that kernel fits.  Measured crossover (bf16,
+    // d = 64, m = 256): it wins from 128 heads up to 512 tokens and from 64
+    // heads up to 384; with fewer heads or longer sequences the segments'
+    // parallelism wins
+    const bool short_seq = BH >= 128 ? s.L <= 512 : BH >= 64 && s.L <= 384;
+    if (segments <= 0 && op == FAVOR_OP_BIDIR && short_seq && favor::bidir_one_kernel(s.dtype == FAVOR_BF16 ? 2 : 4, D, m))
+        nseg = 1;
     if (nseg < 1) nseg = 1;
     if (nseg > tiles) nseg = tiles;
     const int per = (s.L + nseg - 1) / nseg;

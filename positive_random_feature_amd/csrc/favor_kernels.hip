@@ -2088,7 +2088,7 @@ static hipError_t launch_all(const LaunchArgs& a) {
     constexpr int PD_KV = D >= 128 ? 1 : 2;
     // one segment per head: the one-kernel bidirectional path when its
     // operand stages fit beside the sums' static LDS
-    if (a.op == OpKind::Bidir && a.nseg == 1 && a.m <= 256) {
+    if (a.op == OpKind::Bidir && a.nseg == 1 && bidir_one_kernel((int)sizeof(T), D, a.m)) {
         auto kern = bidir_head_kernel<T, D, PD_KV, RELU>;
         static const size_t static_lds = [kern] {
             hipFuncAttributes at{};

@@ -41,4 +41,18 @@ size_t causal_smem_bytes(int dtype_bytes, int D, int m) {
            sizeof(float) * (size_t)c.w * 32 * (D + 4) + sizeof(float) * (size_t)c.w * 32 + sizeof(float) * 2 * 2 * 32;
 }
 
+bool bidir_one_kernel(int dtype_bytes, int D, int m) {
+    // The one-kernel path holds in LDS the segment-sum pass's staged K/V tiles
+    // (three slots of two 64-row tiles, row stride D + 16 / dtype_bytes) and
+    // row norms, the per-block key shifts (16 floats), and the two output
+    // operands (packed [KV | z]^T: (D/16 + 1) m/32 tiles; packed projection:
+    // m/16 max(1, D/32) tiles; 64 lanes x 8 elements each).
+    if (m > 256 || (dtype_bytes == 4 && D >= 128)) return false;
+    const size_t eb = (size_t)dtype_bytes;
+    const size_t ksd = D < 32 ? 1 : (size_t)D / 32;
+    const size_t lds = eb * 3 * 2 * 64 * (size_t)(D + 16 / dtype_bytes) + sizeof(float) * (3 * 64 + 16) +
+                       8 * eb * 64 * ((size_t)(D / 16 + 1) * (m / 32) + (size_t)(m / 16) * ksd);
+    return lds <= kMaxLds;
+}
+
 }  // namespace favor

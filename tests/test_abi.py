@@ -289,6 +289,30 @@ def test_plan_validation(lib):
     assert _causal_plan(lib, s, segments=3, nbytes=need - 1) == WORKSPACE
 
 
+
+@pytest.mark.parametrize("dtype,d,m,BH,L,one", [
+    (_lib.FAVOR_BF16, 64, 256, 128, 512, True),   # the one-kernel path fits
+    (_lib.FAVOR_BF16, 64, 256, 64, 384, True),
+    (_lib.FAVOR_BF16, 128, 64, 128, 512, True),
+    (_lib.FAVOR_F32, 32, 256, 128, 512, True),
+    (_lib.FAVOR_F32, 64, 256, 128, 512, False),   # does not fit: segments kept
+    (_lib.FAVOR_BF16, 128, 256, 128, 512, False),
+    (_lib.FAVOR_BF16, 64, 256, 32, 512, False),   # too few heads
+    (_lib.FAVOR_BF16, 64, 256, 64, 512, False),
+    (_lib.FAVOR_BF16, 64, 256, 128, 1024, False),  # too long
+])
+def test_bidir_plan_one_segment_only_where_one_kernel_runs(lib, dtype, d, m, BH, L, one):
+    """The automatic bidirectional plan gives each head a single segment (one
+    kernel per call) only for many heads of short sequences whose one-kernel
+    path fits a compute unit's LDS; elsewhere it keeps the segments.  The
+    plan is visible through the workspace size, which grows with it."""
+    s = shp(B=BH // 8, H=8, L=L, d=d, m=m, dtype=dtype)
+    auto = lib.favor_workspace_bytes(1, ctypes.byref(s), 0)
+    one_seg = lib.favor_workspace_bytes_plan(1, ctypes.byref(s), ctypes.byref(_lib.plan(0, 1)))
+    assert (auto == one_seg) == one
+    if not one:
+        assert auto > one_seg
+
 def test_noalloc_validation(lib):
     """The entry point without a workspace validates like favor_causal and
     refuses shapes whose workspace exceeds its static scratch array, all

@@ -1,10 +1,12 @@
 """The one-kernel bidirectional path (one workgroup per head computes the
 head's sums and then its outputs), taken when the launch plan gives each head
-a single segment: many heads of short sequences, or an explicit one-segment
-plan.  Every element against the fp64 oracle, for both dtypes, d from 16 to
-128, m up to 256, shared and per-head projections, ragged and one-token
-sequences, ReLU features; and the one-segment plan against a multi-segment
-plan of the same call."""
+a single segment (many heads of short sequences, or an explicit one-segment
+plan) and its operands fit in LDS.  Every element against the fp64 oracle,
+for both dtypes, d from 16 to 128, m up to 256, shared and per-head
+projections, ragged and one-token sequences, ReLU features (the bf16 d = 128,
+m = 128 and fp32 d = 64, m = 128 cases do not fit and run the three kernels on
+the one-segment plan); and the one-segment plan against a multi-segment plan
+of the same call."""
 
 import numpy as np
 import pytest
@@ -37,7 +39,8 @@ def _rel(a, b):
 
 
 @pytest.mark.parametrize("dtype,d,m,B,H,L,per_head,feature", [
-    ("bf16", 64, 256, 8, 8, 512, False, "positive"),
+    ("bf16", 64, 256, 8, 8, 384, False, "positive"),
+    ("bf16", 64, 256, 16, 8, 512, True, "positive"),
     ("bf16", 64, 256, 16, 4, 301, True, "positive"),
     ("bf16", 128, 128, 8, 8, 200, True, "positive"),
     ("bf16", 32, 64, 4, 16, 97, False, "positive"),
