@@ -79,9 +79,13 @@ Plan make_plan(int op, const favor_shape& s, int segments = 0) {
     // d = 64, m = 256): it wins from 128 heads up to 512 tokens and from 64
     // heads up to 384; with fewer heads or longer sequences the segments'
     // parallelism wins
-    const bool short_seq = BH >= 128 ? s.L <= 512 : BH >= 64 && s.L <= 384;
-    if (segments <= 0 && op == FAVOR_OP_BIDIR && short_seq && favor::bidir_one_kernel(s.dtype == FAVOR_BF16 ? 2 : 4, D, m))
-        nseg = 1;
+    const int eb = s.dtype == FAVOR_BF16 ? 2 : 4;
+    bool short_seq = BH >= 128 ? s.L <= 512 : BH >= 64 && s.L <= 384;
+    // with 32 features the key-split kernel keeps all its waves busy: one
+    // segment wins up to 512 tokens at any head count, and up to 4096 from
+    // 128 heads
+    if (favor::bidir_small_shape(eb, D, m)) short_seq = s.L <= 512 || (BH >= 128 && s.L <= 4096);
+    if (segments <= 0 && op == FAVOR_OP_BIDIR && short_seq && favor::bidir_one_kernel(eb, D, m)) nseg = 1;
     if (nseg < 1) nseg = 1;
     if (nseg > tiles) nseg = tiles;
     const int per = (s.L + nseg - 1) / nseg;

@@ -78,8 +78,12 @@ CausalCfg causal_config(int dtype_bytes, int D, int m);
 bool causal_wide_shape(int dtype_bytes, int D, int m);
 // LDS bytes the causal kernel needs (SIZE_MAX when the shape is unsupported).
 size_t causal_smem_bytes(int dtype_bytes, int D, int m);
+// Shapes whose one-segment bidirectional call runs the key-split kernel
+// (m = 32: the waves split the keys instead of the features).
+bool bidir_small_shape(int dtype_bytes, int D, int m);
 // Whether a bidirectional call planned with one segment per head runs as
-// one kernel (its operands and staged tiles fit a compute unit's LDS).
+// one kernel (the key-split kernel, or the feature-split one where its
+// operands and staged tiles fit a compute unit's LDS).
 bool bidir_one_kernel(int dtype_bytes, int D, int m);
 
 }  // namespace favor

@@ -30,6 +30,11 @@
 //                   feature slice, state by value columns)
 //   causal_chunk    per (head, segment), every other shape: chunked scan,
 //                   32 tokens per step, state split by features
+// and, for bidirectional plans with one segment per head, one kernel per call:
+//   bidir_head      per head: the sums by feature-parallel waves, then the
+//                   output pass (m <= 256)
+//   bidir_small     per head, m = 32: the sums by key-parallel waves, then
+//                   the output pass
 // and for the features API:
 //   pack_omega      omega fp32 -> log2(e) omega in operand order
 //   features        phi(x) written to memory
@@ -915,6 +920,237 @@ __global__ __launch_bounds__(512) void bidir_head_kernel(const T* __restrict__ q
         load_queries<T, D>(q, xbase, L, tbase, xq);
         query_consts<T, D, RELU>(xq, cq);
         out_tiles<T, D, RELU>(om_stage, kv_stage, offs, xq, cq, out, xbase, L, nfb, tbase);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bidir_small: the whole bidirectional operation of one head in one
+// workgroup for 32 features (d <= 64 in bf16, d <= 32 in fp32; the kernel
+// takes m = 64 as well, which measured no faster than the feature-split
+// path).  With one segment per head
+// the feature-parallel sums of bidir_head would keep only m/32 of the eight
+// waves busy, so here the waves split the keys instead: wave w takes the
+// 32-token chunks w, w + 8, ..., stages each chunk's K and V rows in LDS
+// tiles of its own, projects the keys over all m features (D[T x F], the
+// projection operands in registers), keeps its own lazily raised shift and
+// accumulates phi(K)^T [V | 1] in registers.  The eight partial sums meet in
+// LDS rescaled to the largest shift (exact up to rounding), are packed into
+// the output operands, and the waves take the head's query tiles through the
+// output loop shared with bidir_out.  Phase-one tiles and phase-two operands
+// share the LDS.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int M>
+struct SmallSmem {
+    static constexpr int RS = LdsTile<T, D>::RS;
+    static constexpr int NT = D / 16 + 1, NFT = M / 16, NFB = M / 32, KSD = D < 32 ? 1 : D / 32;
+    static constexpr size_t TILES = sizeof(T) * (size_t)8 * 2 * 32 * RS;  // K and V chunk of each wave
+    static constexpr size_t NORMS = sizeof(float) * 8 * 32;
+    static constexpr size_t SUMS = sizeof(float) * (size_t)NFT * NT * 64 * 4;  // merged sums, D layout
+    static constexpr size_t KV = sizeof(vec8<T>) * (size_t)NT * NFB * 64;
+    static constexpr size_t OM = sizeof(vec8<T>) * (size_t)NFT * KSD * 64;
+    static constexpr size_t P1 = TILES + NORMS, P2 = SUMS + KV + OM;
+    static constexpr size_t BYTES = P1 > P2 ? P1 : P2;
+};
+
+template <typename T, int D, int M, bool RELU>
+__global__ __launch_bounds__(512) void bidir_small_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                          const T* __restrict__ v, const float* __restrict__ omega,
+                                                          int om_per_head, T* __restrict__ out, int H, int L) {
+    using SM = SmallSmem<T, D, M>;
+    constexpr int RS = SM::RS, NT = SM::NT, NFT = SM::NFT, NFB = SM::NFB, KSD = SM::KSD;
+    constexpr int CPR = D / 8;      // lanes per staged row, 8 elements each
+    constexpr int PIECES = CPR / 2;  // 8-element pieces per lane of a 32-row chunk
+    static_assert(M % 32 == 0 && M <= 64 && D >= 16 && D <= (sizeof(T) == 2 ? 64 : 32), "bidir_small shape");
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    __shared__ float wave_shift[8];
+    __shared__ float offs[NFB];
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int bh = blockIdx.x, h = bh % H;
+    const size_t xbase = (size_t)bh * L * D;
+    const float* omh = omega + (om_per_head ? (size_t)h * M * D : 0);
+    T* kt = reinterpret_cast<T*>(smem_raw) + (size_t)w * 2 * 32 * RS;
+    T* vt = kt + 32 * RS;
+    float* nrm = reinterpret_cast<float*>(smem_raw + SM::TILES) + 32 * w;
+    const int nch = (L + 31) / 32;
+
+    // This lane's pieces of a 32-token chunk of K and V (row clamped to the
+    // sequence: rows past the end are zeroed when staged).
+    vec8<T> ck[PIECES], cv[PIECES];
+    auto load_chunk = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) {
+            const int pc = lane + 64 * i, row = pc / CPR, col = 8 * (pc % CPR);
+            const size_t go = xbase + (size_t)min(32 * c + row, L - 1) * D + col;
+            ck[i] = load8(k + go);
+            cv[i] = load8(v + go);
+        }
+    };
+    // Every load a wave needs first goes out at once: its first chunk of keys
+    // and values, its first query tile, the projection operands.
+    if (w < nch) load_chunk(w);
+    vec8<T> xq[kOutTiles][KSD];
+    const int tq0 = w * 16 * kOutTiles;
+    if (tq0 < L) load_queries<T, D>(q, xbase, L, tq0, xq);
+    vec8<T> om[NFT][KSD];  // projection operands of all M features (B of D[T x F])
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) om[ft][ks] = omega_operand<T, D>(omh, 16 * ft + r, ks, g);
+
+    f4 kv[NFT][NT];
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) kv[ft][nt] = f4splat(0.0f);
+    float Mw = kNegInf;  // this wave's key shift (log2 units); -inf until its first chunk
+    const vec8<T> ones = splat8<T>(1.0f);
+
+    for (int c = w; c < nch; c += 8) {
+        const int t0 = 32 * c;
+        // stage the chunk; rows past the end are zero with the row constant
+        // -inf, so their features vanish
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) {
+            const int pc = lane + 64 * i, row = pc / CPR, col = 8 * (pc % CPR);
+            const bool in = t0 + row < L;
+            const vec8<T> xk = in ? ck[i] : zero8<T>();
+            *reinterpret_cast<vec8<T>*>(kt + row * RS + col) = xk;
+            *reinterpret_cast<vec8<T>*>(vt + row * RS + col) = in ? cv[i] : zero8<T>();
+            const float ss = group_sum<CPR>(sumsq8(xk));
+            if (col == 0) nrm[row] = !in ? kNegInf : RELU ? 0.0f : -0.5f * kLog2e * ss;
+        }
+        // the next chunk of this wave is loaded while this one is computed
+        if (c + 8 < nch) load_chunk(c + 8);
+        // the tiles are this wave's own: ordering its LDS accesses suffices
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // projection of the 32 keys over all M features, relative to Mw
+        f4 p[2][NFT];
+        float lm = kNegInf;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const f4 nr = *reinterpret_cast<const f4*>(nrm + 16 * tt + 4 * g);
+            const f4 init = (RELU || Mw == kNegInf) ? nr : nr - Mw;
+            vec8<T> x[KSD];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) x[ks] = row_operand<T, D>(kt, 16 * tt + r, ks, g);
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) {
+                p[tt][ft] = init;
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) p[tt][ft] = mma32(x[ks], om[ft][ks], p[tt][ft]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lm = __builtin_fmaxf(lm, p[tt][ft][i]);
+            }
+        }
+        if (RELU) {
+            Mw = 0.0f;
+        } else if (Mw == kNegInf || wave_any(lm > kTau)) {
+            // first chunk of the wave: its maximum becomes the shift (the chunk
+            // holds at least one key); later: raise it, rescaling the sums
+            const float tm = wave_max_uniform(lm);
+            if (Mw != kNegInf) {
+                const float sc = exp2f_fast(-tm);
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) kv[ft][nt] *= sc;
+            }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft) p[tt][ft] -= tm;
+            Mw = Mw == kNegInf ? tm : Mw + tm;
+        }
+        // features as the A operand (lane = feature, the 32 keys in kappa
+        // order) and the update of the sums
+        vec8<T> a[NFT];
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+            f4 e0, e1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e0[i] = feat<RELU>(p[0][ft][i]);
+                e1[i] = feat<RELU>(p[1][ft][i]);
+            }
+            a[ft] = pack8t<T>(e0, e1);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT - 1; ++nt) {
+            const vec8<T> vb = kappa_col<RS>(vt, 16 * nt, lane);
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) kv[ft][nt] = mma32(a[ft], vb, kv[ft][nt]);
+        }
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) kv[ft][NT - 1] = mma32(a[ft], ones, kv[ft][NT - 1]);
+        // the next chunk's staging reuses the tiles
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // the waves' sums, rescaled to the largest shift, accumulated in LDS one
+    // wave after another (the tiles are dead: the space becomes the sums)
+    if (lane == 0) wave_shift[w] = Mw;
+    __syncthreads();
+    float Mall = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Mall = __builtin_fmaxf(Mall, wave_shift[i]);
+    const float sc = Mw == kNegInf ? 0.0f : exp2f_fast(Mw - Mall);
+    float* sums = reinterpret_cast<float*>(smem_raw);
+    for (int rw = 0; rw < 8; ++rw) {
+        if (w == rw) {
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    f4* sp = reinterpret_cast<f4*>(sums + ((size_t)(ft * NT + nt) * 64 + lane) * 4);
+                    *sp = (rw == 0 ? f4splat(0.0f) : *sp) + sc * kv[ft][nt];
+                }
+        }
+        __syncthreads();
+    }
+
+    // output operands: [KV | z]^T block-major, and the packed projection
+    // (which is every wave's register operand: wave 0 stores its copy); one
+    // shift for all keys, so no block offsets
+    typedef __attribute__((ext_vector_type(4))) T T4;
+    vec8<T>* kv_stage = reinterpret_cast<vec8<T>*>(smem_raw + SM::SUMS);
+    vec8<T>* om_stage = kv_stage + (size_t)NT * NFB * 64;
+    for (int e = threadIdx.x; e < NFB * NT * 64 * 2; e += blockDim.x) {
+        const int half = e & 1, ln = (e >> 1) & 63, mt = (e >> 7) % NT, fb = (e >> 7) / NT;
+        const f4 x = *reinterpret_cast<const f4*>(sums + ((size_t)((2 * fb + half) * NT + mt) * 64 + ln) * 4);
+        T4 pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = (T)x[i];
+        reinterpret_cast<T4*>(kv_stage + ((size_t)fb * NT + mt) * 64 + ln)[half] = pk;
+    }
+    if (w == 0) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) om_stage[(ft * KSD + ks) * 64 + lane] = om[ft][ks];
+    }
+    if ((int)threadIdx.x < NFB) offs[threadIdx.x] = 0.0f;
+    __syncthreads();
+
+    // the query tiles, each one's successor loaded while it is computed
+    for (int tb = tq0; tb < L; tb += 8 * 16 * kOutTiles) {
+        float cq[kOutTiles];
+        query_consts<T, D, RELU>(xq, cq);
+        const bool more = tb + 8 * 16 * kOutTiles < L;
+        vec8<T> xn[kOutTiles][KSD];
+        if (more) load_queries<T, D>(q, xbase, L, tb + 8 * 16 * kOutTiles, xn);
+        out_tiles<T, D, RELU>(om_stage, kv_stage, offs, xq, cq, out, xbase, L, NFB, tb);
+        if (more) {
+#pragma unroll
+            for (int tt = 0; tt < kOutTiles; ++tt)
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) xq[tt][ks] = xn[tt][ks];
+        }
     }
 }
 
@@ -2060,6 +2296,16 @@ static hipError_t launch_causal_wide(const LaunchArgs& a, const bf16x8* ompack, 
     return hipGetLastError();
 }
 
+template <typename T, int D, int M, bool RELU>
+static hipError_t launch_bidir_small(const LaunchArgs& a, const T* q, const T* k, const T* v, T* out, int per_head) {
+    constexpr size_t bytes = SmallSmem<T, D, M>::BYTES;
+    static_assert(bytes + sizeof(float) * 16 <= kMaxLds, "bidir_small LDS");
+    auto kern = bidir_small_kernel<T, D, M, RELU>;
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(512), bytes, a.stream, q, k, v, a.omega, per_head, out, a.H, a.L);
+    return hipGetLastError();
+}
+
 template <typename T, int D, bool RELU>
 static hipError_t launch_all(const LaunchArgs& a) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
@@ -2086,6 +2332,15 @@ static hipError_t launch_all(const LaunchArgs& a) {
     const int nfg = (a.m + 255) / 256;
     stage_event(a, 0);
     constexpr int PD_KV = D >= 128 ? 1 : 2;
+    // one segment per head and 32 features: the key-split one-kernel path
+    // (fp32 with d = 64 would not fit its registers)
+    if constexpr (sizeof(T) == 2 ? D <= 64 : D <= 32) {
+        if (a.op == OpKind::Bidir && a.nseg == 1 && bidir_small_shape((int)sizeof(T), D, a.m)) {
+            const hipError_t err = launch_bidir_small<T, D, 32, RELU>(a, q, k, v, out, per_head);
+            for (int i = 1; i <= 3; ++i) stage_event(a, i);
+            return err;
+        }
+    }
     // one segment per head: the one-kernel bidirectional path when its
     // operand stages fit beside the sums' static LDS
     if (a.op == OpKind::Bidir && a.nseg == 1 && bidir_one_kernel((int)sizeof(T), D, a.m)) {

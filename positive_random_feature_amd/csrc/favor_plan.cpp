@@ -41,12 +41,19 @@ size_t causal_smem_bytes(int dtype_bytes, int D, int m) {
            sizeof(float) * (size_t)c.w * 32 * (D + 4) + sizeof(float) * (size_t)c.w * 32 + sizeof(float) * 2 * 2 * 32;
 }
 
+bool bidir_small_shape(int dtype_bytes, int D, int m) {
+    // the key-split one-kernel path: every wave sums all 32 features over its
+    // own keys (its sums and operands fit the registers for these d)
+    return m == 32 && (dtype_bytes == 2 ? D <= 64 : D <= 32);
+}
+
 bool bidir_one_kernel(int dtype_bytes, int D, int m) {
     // The one-kernel path holds in LDS the segment-sum pass's staged K/V tiles
     // (three slots of two 64-row tiles, row stride D + 16 / dtype_bytes) and
     // row norms, the per-block key shifts (16 floats), and the two output
     // operands (packed [KV | z]^T: (D/16 + 1) m/32 tiles; packed projection:
     // m/16 max(1, D/32) tiles; 64 lanes x 8 elements each).
+    if (bidir_small_shape(dtype_bytes, D, m)) return true;
     if (m > 256 || (dtype_bytes == 4 && D >= 128)) return false;
     const size_t eb = (size_t)dtype_bytes;
     const size_t ksd = D < 32 ? 1 : (size_t)D / 32;

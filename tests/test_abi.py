@@ -300,14 +300,21 @@ def test_plan_validation(lib):
     (_lib.FAVOR_BF16, 64, 256, 32, 512, False),   # too few heads
     (_lib.FAVOR_BF16, 64, 256, 64, 512, False),
     (_lib.FAVOR_BF16, 64, 256, 128, 1024, False),  # too long
+    (_lib.FAVOR_F32, 16, 32, 1, 256, True),       # 32 features: the key-split kernel
+    (_lib.FAVOR_BF16, 64, 32, 8, 512, True),
+    (_lib.FAVOR_BF16, 32, 32, 128, 4096, True),
+    (_lib.FAVOR_BF16, 32, 32, 64, 1024, False),
+    (_lib.FAVOR_F32, 64, 32, 1, 256, False),      # fp32 d = 64: not that kernel, too few heads
 ])
 def test_bidir_plan_one_segment_only_where_one_kernel_runs(lib, dtype, d, m, BH, L, one):
     """The automatic bidirectional plan gives each head a single segment (one
     kernel per call) only for many heads of short sequences whose one-kernel
     path fits a compute unit's LDS; elsewhere it keeps the segments.  The
     plan is visible through the workspace size, which grows with it."""
-    s = shp(B=BH // 8, H=8, L=L, d=d, m=m, dtype=dtype)
+    B, H = (BH // 8, 8) if BH >= 8 else (1, BH)
+    s = shp(B=B, H=H, L=L, d=d, m=m, dtype=dtype)
     auto = lib.favor_workspace_bytes(1, ctypes.byref(s), 0)
+    assert auto > 0
     one_seg = lib.favor_workspace_bytes_plan(1, ctypes.byref(s), ctypes.byref(_lib.plan(0, 1)))
     assert (auto == one_seg) == one
     if not one:
