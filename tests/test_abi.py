@@ -320,6 +320,16 @@ def test_bidir_plan_one_segment_only_where_one_kernel_runs(lib, dtype, d, m, BH,
     if not one:
         assert auto > one_seg
 
+
+@pytest.mark.parametrize("B,H,L,segs", [(2, 8, 512, 8), (1, 8, 1024, 16), (2, 8, 8192, 16), (1, 1, 100, 1)])
+def test_causal_plan_segments_of_at_least_64_tokens(lib, B, H, L, segs):
+    """The automatic causal plan keeps segments of at least 64 tokens (and
+    one per compute unit otherwise); visible through the workspace size."""
+    s = shp(B=B, H=H, L=L)
+    auto = lib.favor_workspace_bytes(2, ctypes.byref(s), 0)
+    want = lib.favor_workspace_bytes_plan(2, ctypes.byref(s), ctypes.byref(_lib.plan(0, segs)))
+    assert auto == want > 0
+
 def test_noalloc_validation(lib):
     """The entry point without a workspace validates like favor_causal and
     refuses shapes whose workspace exceeds its static scratch array, all
