@@ -66,6 +66,8 @@ SHAPES = [  # (base workload, d, m, B, H, L, dtype)
     ("causal_bf16_8k", 32, 64, 1, 2, 65, "bf16"),
     ("bidir_f32_tiny", 16, 32, 1, 2, 131, "f32"),
     ("bidir_f32_tiny", 64, 256, 1, 1, 1, "f32"),
+    ("causal_bf16_8k", 32, 32, 1, 2, 300, "bf16"),     # bidirectional: the key-split one-kernel path
+    ("causal_bf16_8k", 64, 256, 16, 8, 200, "bf16"),   # bidirectional: the feature-split one-kernel path
 ]
 
 
@@ -147,6 +149,28 @@ def test_nan_propagation(d, m, op, where, t):
         nan_want = nan_want.copy()
         nan_want[0, 1, c0:t, d // 2 + 3] = True
     print(f"[safety] NaN in {where}[{t}] {op} d={d} m={m}: {int(nan_want.sum())} NaN expected, "
+          f"{int(nan_got.sum())} produced", flush=True)
+    assert nan_want.any()
+    np.testing.assert_array_equal(nan_got, nan_want)
+    ok = ~nan_want
+    assert np.isfinite(got[ok]).all()
+    assert _rel(got[ok], want[ok]) <= 2e-2
+
+
+@pytest.mark.parametrize("d,m", [(32, 32), (64, 256)])
+@pytest.mark.parametrize("where,t", [("k", 300), ("k", 0), ("q", 255), ("v", 411), ("k", 499)])
+def test_nan_propagation_one_kernel(d, m, where, t):
+    """The same NaN pattern through the one-kernel bidirectional paths (a
+    one-segment plan: m = 32 runs the key-split kernel, m = 256 the
+    feature-split one): a NaN key reaches every row of its head, a NaN query
+    only its row, a NaN value that column of every row."""
+    B, H, L = 1, 3, 500
+    vals, dev, om = _nan_case(d, m, B, H, L, where, t, col=d // 2 + 3)
+    got = favor.bidir(*dev, torch.from_numpy(om).to(DEV), segments=1).float().cpu().numpy().astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        want = native.bidir(*vals, om)
+    nan_want, nan_got = np.isnan(want), np.isnan(got)
+    print(f"[safety] NaN in {where}[{t}] one-kernel bidir d={d} m={m}: {int(nan_want.sum())} NaN expected, "
           f"{int(nan_got.sum())} produced", flush=True)
     assert nan_want.any()
     np.testing.assert_array_equal(nan_got, nan_want)
