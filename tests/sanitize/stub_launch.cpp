@@ -1,14 +1,15 @@
 // Host-only stand-in for the kernel launcher, for the sanitizer build of the
 // C ABI (favor_api.cpp, favor_plan.cpp): instead of launching kernels it
 // checks the launch plan and the workspace layout the ABI computed, against
-// the bounds the driver registered for the call.  Test infrastructure only.
+// the bounds the test program (abi_driver.cpp) registered for the call.  Test
+// infrastructure only.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 
 #include "../../positive_random_feature_amd/csrc/favor_kernels.h"
 
-// set by the driver before each call that should reach a launch
+// set by the test program before each call that should reach a launch
 extern "C" {
 const char* g_ws_base = nullptr;
 size_t g_ws_bytes = 0;
