@@ -160,10 +160,15 @@ favor_status favor_causal(const favor_shape *shape, const void *q, const void *k
  *   chunk:    causal chunk length as for favor_causal (0 = default);
  *             ignored by bidirectional attention.
  *   segments: token segments per head, 0 = automatic (sized so that one
- *             pass fills 256 compute units), else 1..256.  Segments are whole
- *             32- or 64-token steps, so fewer may be used than requested
- *             (at most ceil(L / 32)).  Negative or > 256:
- *             FAVOR_ERR_INVALID_ARG.
+ *             pass fills 256 compute units, with segments of at least 256
+ *             tokens for bidirectional m >= 128 and 64 tokens for causal;
+ *             one per head for many heads of short bidirectional sequences
+ *             and for m = 32 up to 512 tokens, where the whole call then
+ *             runs as one kernel), else 1..256.  A bidirectional plan with
+ *             one segment runs as one kernel wherever that kernel's operands
+ *             fit on a compute unit.  Segments are whole 32- or 64-token
+ *             steps, so fewer may be used than requested (at most
+ *             ceil(L / 32)).  Negative or > 256: FAVOR_ERR_INVALID_ARG.
  * A NULL plan means both defaults.  The workspace size depends on the plan:
  * favor_workspace_bytes_plan returns it (0 for an invalid shape or plan).
  * The other arguments are those of favor_bidir / favor_causal.
