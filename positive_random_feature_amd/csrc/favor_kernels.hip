@@ -945,7 +945,8 @@ struct SmallSmem {
     static constexpr int NT = D / 16 + 1, NFT = M / 16, NFB = M / 32, KSD = D < 32 ? 1 : D / 32;
     static constexpr size_t TILES = sizeof(T) * (size_t)8 * 2 * 32 * RS;  // K and V chunk of each wave
     static constexpr size_t NORMS = sizeof(float) * 8 * 32;
-    static constexpr size_t SUMS = sizeof(float) * (size_t)NFT * NT * 64 * 4;  // merged sums, D layout
+    static constexpr size_t SLOT = (size_t)NFT * NT * 64 * 4;  // one wave's sums (floats, D layout)
+    static constexpr size_t SUMS = sizeof(float) * 8 * SLOT;
     static constexpr size_t KV = sizeof(vec8<T>) * (size_t)NT * NFB * 64;
     static constexpr size_t OM = sizeof(vec8<T>) * (size_t)NFT * KSD * 64;
     static constexpr size_t P1 = TILES + NORMS, P2 = SUMS + KV + OM;
@@ -1092,37 +1093,35 @@ __global__ __launch_bounds__(512) void bidir_small_kernel(const T* __restrict__ 
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // the waves' sums, rescaled to the largest shift, accumulated in LDS one
-    // wave after another (the tiles are dead: the space becomes the sums)
+    // each wave's sums, rescaled to the largest shift, into a slot of its own
+    // (the tiles are dead: the space becomes the slots)
     if (lane == 0) wave_shift[w] = Mw;
     __syncthreads();
     float Mall = kNegInf;
 #pragma unroll
     for (int i = 0; i < 8; ++i) Mall = __builtin_fmaxf(Mall, wave_shift[i]);
     const float sc = Mw == kNegInf ? 0.0f : exp2f_fast(Mw - Mall);
-    float* sums = reinterpret_cast<float*>(smem_raw);
-    for (int rw = 0; rw < 8; ++rw) {
-        if (w == rw) {
+    float* slots = reinterpret_cast<float*>(smem_raw);
 #pragma unroll
-            for (int ft = 0; ft < NFT; ++ft)
+    for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    f4* sp = reinterpret_cast<f4*>(sums + ((size_t)(ft * NT + nt) * 64 + lane) * 4);
-                    *sp = (rw == 0 ? f4splat(0.0f) : *sp) + sc * kv[ft][nt];
-                }
-        }
-        __syncthreads();
-    }
+        for (int nt = 0; nt < NT; ++nt)
+            *reinterpret_cast<f4*>(slots + w * SM::SLOT + ((size_t)(ft * NT + nt) * 64 + lane) * 4) = sc * kv[ft][nt];
+    __syncthreads();
 
-    // output operands: [KV | z]^T block-major, and the packed projection
-    // (which is every wave's register operand: wave 0 stores its copy); one
-    // shift for all keys, so no block offsets
+    // output operands: [KV | z]^T block-major, the eight slots added in wave
+    // order as they are packed, and the packed projection (which is every
+    // wave's register operand: wave 0 stores its copy); one shift for all
+    // keys, so no block offsets
     typedef __attribute__((ext_vector_type(4))) T T4;
     vec8<T>* kv_stage = reinterpret_cast<vec8<T>*>(smem_raw + SM::SUMS);
     vec8<T>* om_stage = kv_stage + (size_t)NT * NFB * 64;
     for (int e = threadIdx.x; e < NFB * NT * 64 * 2; e += blockDim.x) {
         const int half = e & 1, ln = (e >> 1) & 63, mt = (e >> 7) % NT, fb = (e >> 7) / NT;
-        const f4 x = *reinterpret_cast<const f4*>(sums + ((size_t)((2 * fb + half) * NT + mt) * 64 + ln) * 4);
+        const float* sp = slots + ((size_t)((2 * fb + half) * NT + mt) * 64 + ln) * 4;
+        f4 x = *reinterpret_cast<const f4*>(sp);
+#pragma unroll
+        for (int i = 1; i < 8; ++i) x += *reinterpret_cast<const f4*>(sp + i * SM::SLOT);
         T4 pk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) pk[i] = (T)x[i];
