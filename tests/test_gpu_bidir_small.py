@@ -95,3 +95,23 @@ def test_against_segmented_plan():
     one = favor.bidir(q, k, v, om, segments=1).float()
     many = favor.bidir(q, k, v, om, segments=6).float()
     assert float((one - many).norm() / many.norm()) <= 1e-2
+
+
+@pytest.mark.parametrize("B,H", [(16, 8), (127, 1)])
+def test_plan_limit(B, H):
+    """The automatic plan at its limit for 32 features: 128 heads of 4096
+    tokens take the key-split kernel (one segment per head), 127 heads of
+    the same length keep the segmented kernels; every element against the
+    oracle either way."""
+    w = WORKLOADS["bidir_bf16_4k"].replace(d=32, m=32, omega_per_head=False)
+    inp = make_inputs(w, B=B, H=H, L=4096, seed=21)
+    om = ref.orf_omega(21, 1, 32, 32)[0]
+    q, k, v = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(DEV)
+               for b in (inp.q_bits, inp.k_bits, inp.v_bits))
+    got = favor.bidir(q, k, v, torch.from_numpy(np.ascontiguousarray(om)).to(DEV))
+    got = got.float().cpu().numpy().astype(np.float64)
+    want = native.bidir(inp.q, inp.k, inp.v, om)
+    err = _rel(got, want)
+    worst = max(_rel(got[b, h], want[b, h]) for b in range(B) for h in range(H))
+    print(f"[bidir_small] plan limit {B}x{H}x4096 d=32 m=32: rel L2 {err:.3e}, worst head {worst:.3e}", flush=True)
+    assert err <= TOL["bf16"] and worst <= TOL["bf16"]
