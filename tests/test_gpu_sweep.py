@@ -87,3 +87,31 @@ def test_random_shape(case):
     err = float(np.linalg.norm(got - want) / np.linalg.norm(want))
     print(f"[sweep] {_id(case)}: rel L2 {err:.3e} (tol {TOL[dtype]})", flush=True)
     assert err <= TOL[dtype]
+
+
+def _draw_many_head_cases(n, seed=20261203):
+    """Bidirectional calls with many heads of short sequences: the range where
+    the automatic plan gives each head one segment and the call runs as one
+    kernel (key-split for m = 32, feature-split where its operands fit), and
+    just around it."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = str(rng.choice(["bf16", "bf16", "f32"]))
+        d = int(rng.choice([16, 32, 64, 128] if dtype == "bf16" else [16, 32, 64]))
+        feature = str(rng.choice(["positive", "positive", "relu"]))
+        m = int(rng.choice([32, 32, 64, 128, 256]))
+        B = int(rng.integers(8, 40))
+        H = int(rng.integers(8, 9))
+        L = int(rng.integers(1, 640))
+        per_head = bool(rng.integers(0, 2))
+        cases.append((100 + i, dtype, d, m, "bidir", feature, B, H, L, per_head))
+    return cases
+
+
+MANY_HEAD_CASES = _draw_many_head_cases(16)
+
+
+@pytest.mark.parametrize("case", MANY_HEAD_CASES, ids=[_id(c) for c in MANY_HEAD_CASES])
+def test_random_many_head_shape(case):
+    test_random_shape(case)
