@@ -266,7 +266,8 @@ template <typename T, int D, int PD, bool RELU>
 __device__ __forceinline__ void kv_partial_block(const T* __restrict__ k, const T* __restrict__ v,
                                                  const float* __restrict__ omega, int om_per_head,
                                                  T* __restrict__ partial, float* __restrict__ pmax, int H, int L,
-                                                 int m, int seg_len, int nseg, int seg, int bh, int fgroup) {
+                                                 int m, int seg_len, int nseg, int seg, int bh, int fgroup,
+                                                 vec8<T>* __restrict__ om_out = nullptr) {
     using TL = LdsTile<T, D>;
     constexpr int RS = TL::RS;
     constexpr int KSD = D < 32 ? 1 : D / 32;
@@ -296,6 +297,15 @@ __device__ __forceinline__ void kv_partial_block(const T* __restrict__ k, const 
     for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) om[ft][ks] = omega_operand<T, D>(omh, (active ? f0 : 0) + 16 * ft + r, ks, g);
+    // the packed projection for the causal scan, when no merge pass follows
+    // to pack it (first segment of each projection's first head)
+    if (om_out && active && seg == 0 && (om_per_head ? bh < H : bh == 0)) {
+        vec8<T>* dst = om_out + (size_t)(om_per_head ? h : 0) * (m / 16) * KSD * 64;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) dst[((size_t)(f0 / 16 + ft) * KSD + ks) * 64 + lane] = om[ft][ks];
+    }
 
     f4 kv[NFT][NT];
 #pragma unroll
@@ -474,9 +484,10 @@ template <typename T, int D, int PD, bool RELU>
 __global__ __launch_bounds__(512) void kv_partial_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                          const float* __restrict__ omega, int om_per_head,
                                                          T* __restrict__ partial, float* __restrict__ pmax, int H,
-                                                         int L, int m, int seg_len, int nseg) {
+                                                         int L, int m, int seg_len, int nseg,
+                                                         vec8<T>* __restrict__ om_out) {
     kv_partial_block<T, D, PD, RELU>(k, v, omega, om_per_head, partial, pmax, H, L, m, seg_len, nseg, blockIdx.x,
-                                     blockIdx.y, blockIdx.z);
+                                     blockIdx.y, blockIdx.z, om_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -1269,7 +1280,7 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
 #pragma unroll
     for (int b = 0; b < KSF; ++b) M = __builtin_fmaxf(M, cm[f0 / 32 + b]);
     f4 G[NFT][NT];
-    {
+    if (carry) {
         const T* cb = carry + ((size_t)bh * nseg + seg) * (size_t)m * D1;
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft) {
@@ -1282,6 +1293,11 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
                 G[ft][nt] = sc * load4f(cb + o);
             }
         }
+    } else {  // no carry: the scan starts from a zero state
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) G[ft][nt] = f4splat(0.0f);
     }
 
     for (int i0 = 0; i0 < nchunks; i0 += PD) {
@@ -1539,7 +1555,12 @@ __global__ __launch_bounds__(512) void causal_tile_kernel(const bf16* __restrict
     for (int b = 0; b < NFB; ++b) Mseg = __builtin_fmaxf(Mseg, cm[b]);
     f4 G[NFT];
     f4 Z[2 * ZB];
-    if (!qwave) {
+    if (!qwave && !carry) {  // no carry: the scan starts from a zero state
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) G[ft] = f4splat(0.0f);
+#pragma unroll
+        for (int zb = 0; zb < 2 * ZB; ++zb) Z[zb] = f4splat(0.0f);
+    } else if (!qwave) {
         const bf16* cb = carry + ((size_t)bh * nseg + seg) * (size_t)M * D1;
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft) {
@@ -1963,7 +1984,12 @@ __global__ __launch_bounds__(512) void causal_wide_kernel(const bf16* __restrict
     for (int b = 0; b < NFB; ++b) Mseg = __builtin_fmaxf(Mseg, cm[b]);
     f4 G[GFT];
     f4 Z[PFT];
-    {
+    if (!carry) {  // no carry: the scan starts from a zero state
+#pragma unroll
+        for (int i = 0; i < GFT; ++i) G[i] = f4splat(0.0f);
+#pragma unroll
+        for (int f = 0; f < PFT; ++f) Z[f] = f4splat(0.0f);
+    } else {
         const bf16* cb = carry + ((size_t)bh * nseg + seg) * (size_t)M * D1;
 #pragma unroll
         for (int i = 0; i < GFT; ++i) {
@@ -2240,6 +2266,20 @@ static inline void stage_event(const LaunchArgs& a, int i) {
     if (a.events) (void)hipEventRecord(static_cast<hipEvent_t>(a.events[i]), a.stream);
 }
 
+// A carry-free causal call: one segment per head and no carried state.  Its
+// merge pass is skipped: the scan starts from a zero state and takes the
+// segment-sum pass's key shifts (for one segment the layout of the merged
+// shifts, [head][segment][block]), and the segment-sum pass packs the
+// projection operands the merge pass would have packed.
+static bool causal_carry_free(const LaunchArgs& a) {
+    return a.op == OpKind::Causal && a.nseg == 1 && !a.state_in && !a.state_out;
+}
+template <typename T>
+static const T* scan_carry(const LaunchArgs& a) {
+    return causal_carry_free(a) ? nullptr : static_cast<const T*>(a.ws_carry);
+}
+static const float* scan_shifts(const LaunchArgs& a) { return causal_carry_free(a) ? a.ws_pmax : a.ws_cmax; }
+
 template <typename T, int D, int FW, int W, bool RELU>
 static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long long om_head_vecs, const T* q,
                                 const T* k, const T* v, T* out) {
@@ -2258,7 +2298,7 @@ static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long
         auto kern = causal_chunk_kernel<T, D, FW, W, 2, PD, OM_REGS, RELU>;
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)two);
         hipLaunchKernelGGL(kern, grid, block, two, a.stream, q, k, v, ompack, om_head_vecs,
-                           static_cast<const T*>(a.ws_carry), a.ws_cmax, out, a.H, a.L, a.m, a.seg_len, a.nseg);
+                           scan_carry<T>(a), scan_shifts(a), out, a.H, a.L, a.m, a.seg_len, a.nseg);
     } else if constexpr (CausalSmem<T, D, FW, W, 1>::BYTES > kMaxLds) {
         return hipErrorInvalidValue;  // rejected by argument validation before any launch
     } else {
@@ -2266,7 +2306,7 @@ static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long
         auto kern = causal_chunk_kernel<T, D, FW, W, 1, PD, OM_REGS, RELU>;
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)one);
         hipLaunchKernelGGL(kern, grid, block, one, a.stream, q, k, v, ompack, om_head_vecs,
-                           static_cast<const T*>(a.ws_carry), a.ws_cmax, out, a.H, a.L, a.m, a.seg_len, a.nseg);
+                           scan_carry<T>(a), scan_shifts(a), out, a.H, a.L, a.m, a.seg_len, a.nseg);
     }
     return hipGetLastError();
 }
@@ -2279,7 +2319,7 @@ static hipError_t launch_causal_tile(const LaunchArgs& a, const bf16x8* ompack, 
     auto kern = causal_tile_kernel<M, RELU>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H), dim3(512), bytes, a.stream, q, k, v, ompack, om_head_vecs,
-                       static_cast<const bf16*>(a.ws_carry), a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
+                       scan_carry<bf16>(a), scan_shifts(a), out, a.H, a.L, a.seg_len, a.nseg);
     return hipGetLastError();
 }
 
@@ -2291,7 +2331,7 @@ static hipError_t launch_causal_wide(const LaunchArgs& a, const bf16x8* ompack, 
     auto kern = causal_wide_kernel<M, RELU>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     hipLaunchKernelGGL(kern, dim3(a.nseg, a.B * a.H, 2), dim3(512), bytes, a.stream, q, k, v, ompack, om_head_vecs,
-                       static_cast<const bf16*>(a.ws_carry), a.ws_cmax, out, a.H, a.L, a.seg_len, a.nseg);
+                       scan_carry<bf16>(a), scan_shifts(a), out, a.H, a.L, a.seg_len, a.nseg);
     return hipGetLastError();
 }
 
@@ -2360,15 +2400,17 @@ static hipError_t launch_all(const LaunchArgs& a) {
         }
     }
     hipLaunchKernelGGL((kv_partial_kernel<T, D, PD_KV, RELU>), dim3(a.nseg, BH, nfg), dim3(512), 0, st, k, v, a.omega, per_head,
-                       reinterpret_cast<T*>(a.ws_partial), a.ws_pmax, a.H, a.L, a.m, a.seg_len, a.nseg);
+                       reinterpret_cast<T*>(a.ws_partial), a.ws_pmax, a.H, a.L, a.m, a.seg_len, a.nseg,
+                       causal_carry_free(a) ? ompack : nullptr);
     stage_event(a, 1);
     const int nfb = a.m / 32;
     const int mode = a.op == OpKind::Bidir ? 0 : 1;
-    hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(nfb, BH, 2), dim3(64 * (D / 16 + 1)), 0, st,
-                       reinterpret_cast<const T*>(a.ws_partial), a.ws_pmax,
-                       a.omega, per_head, a.H, a.m, a.nseg, mode, reinterpret_cast<vec8<T>*>(a.ws_kvpack), a.ws_mmax,
-                       static_cast<T*>(a.ws_carry), a.ws_cmax, ompack, mode == 1 ? a.state_in : nullptr,
-                       mode == 1 ? a.state_out : nullptr);
+    if (!causal_carry_free(a)) {
+        hipLaunchKernelGGL((merge_scan_kernel<T, D>), dim3(nfb, BH, 2), dim3(64 * (D / 16 + 1)), 0, st,
+                           reinterpret_cast<const T*>(a.ws_partial), a.ws_pmax, a.omega, per_head, a.H, a.m, a.nseg,
+                           mode, reinterpret_cast<vec8<T>*>(a.ws_kvpack), a.ws_mmax, static_cast<T*>(a.ws_carry),
+                           a.ws_cmax, ompack, mode == 1 ? a.state_in : nullptr, mode == 1 ? a.state_out : nullptr);
+    }
     stage_event(a, 2);
     if (a.op == OpKind::Bidir) {
         constexpr int NTT = 2;

@@ -118,3 +118,26 @@ def test_workspace_follows_plan():
     favor.causal(q, k, v, om_d, segments=1, workspace=small)   # enough for one segment
     with pytest.raises(ValueError, match="workspace"):
         favor.causal(q, k, v, om_d, workspace=small)
+
+
+@pytest.mark.parametrize("d,m,dtype,relu", [(64, 256, "bf16", False), (64, 256, "bf16", True), (128, 256, "bf16", False),
+                                              (32, 64, "bf16", False), (32, 64, "f32", False)])
+def test_causal_one_segment_per_head(d, m, dtype, relu):
+    """Causal calls with one segment per head and no carried state skip the
+    merge pass: the scan starts from a zero state with the segment-sum
+    pass's key shifts, and that pass packs the projection operands.  256
+    heads take that plan automatically; every element against the oracle
+    (the tile scan, the d = 128 scan and the generic one), and equal to the
+    same call forced to two segments up to rounding."""
+    B, H, L = 32, 8, 150
+    _, inp, om, (q, k, v), omd = _case("causal_bf16_8k", d, m, B, H, L, dtype=dtype)
+    feature = "relu" if relu else "positive"
+    got = favor.causal(q, k, v, omd, feature=feature).float()
+    two = favor.causal(q, k, v, omd, feature=feature, segments=2).float()
+    g = got.cpu().numpy().astype(np.float64)
+    want = ref.causal(inp.q, inp.k, inp.v, om, kind="relu") if relu else native.causal(inp.q, inp.k, inp.v, om)
+    err, worst = _rel(g, want), _worst_tile(g, want)
+    print(f"[plan] causal one segment per head d={d} m={m} {dtype} {feature} {B}x{H}x{L}: rel L2 {err:.3e}, "
+          f"worst tile {worst:.3e}", flush=True)
+    assert err <= TOL[dtype] and worst <= TOL[dtype]
+    assert float((got - two).norm() / two.norm()) <= (1e-2 if dtype == "bf16" else 1e-5)
