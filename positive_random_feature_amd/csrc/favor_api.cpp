@@ -99,13 +99,13 @@ Plan make_plan(int op, const favor_shape& s, int segments = 0) {
     p.nseg = (s.L + p.seg_len - 1) / p.seg_len;
     const size_t rows = (size_t)BH * p.nseg * m;
     // segment sums in the input type (bf16 sums feed bf16 operands downstream)
-    p.partial = align256(rows * (D + 1) * (s.dtype == FAVOR_BF16 ? 2 : sizeof(float)));
+    p.partial = align256(rows * (D + 1) * (size_t)eb);
     p.pmax = align256((size_t)BH * p.nseg * (m / 32) * sizeof(float));
     if (op == FAVOR_OP_BIDIR) {
         p.kvpack = align256((size_t)BH * (D / 16 + 1) * (m / 32) * 64 * vec8);
         p.mmax = align256((size_t)BH * (m / 32) * sizeof(float));
     } else {
-        p.carry = align256(rows * (D + 1) * (s.dtype == FAVOR_BF16 ? 2 : sizeof(float)));
+        p.carry = align256(rows * (D + 1) * (size_t)eb);  // causal carries, in the input type too
         p.cmax = align256((size_t)BH * p.nseg * (m / 32) * sizeof(float));
     }
     p.total = p.ompack + p.partial + p.pmax + p.kvpack + p.mmax + p.carry + p.cmax;
