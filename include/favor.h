@@ -163,8 +163,9 @@ favor_status favor_causal(const favor_shape *shape, const void *q, const void *k
  *             pass fills 256 compute units, with segments of at least 256
  *             tokens for bidirectional m >= 128 and 64 tokens for causal;
  *             one per head for many heads of short bidirectional sequences
- *             and for m = 32 up to 512 tokens, where the whole call then
- *             runs as one kernel), else 1..256.  A bidirectional plan with
+ *             (from 128 heads up to 512 tokens, from 64 up to 384) and,
+ *             with m = 32, up to 512 tokens, or 4096 from 128 heads: the
+ *             whole call then runs as one kernel), else 1..256.  A bidirectional plan with
  *             one segment runs as one kernel wherever that kernel's operands
  *             fit on a compute unit.  Segments are whole 32- or 64-token
  *             steps, so fewer may be used than requested (at most
