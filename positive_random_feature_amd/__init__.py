@@ -155,7 +155,8 @@ def bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, omega: torch.Tensor
     ``segments``: token segments per head of the reduction (0 = automatic);
     with one segment per head the call runs as a single kernel where its
     operands fit on a compute unit (the automatic plan chooses that for many
-    heads of short sequences, and for m = 32 up to 512 tokens)."""
+    heads of short sequences, and for m = 32 up to 512 tokens, or up to 4096
+    from 128 heads)."""
     dev, dt = _check_inputs([q, k, v], omega, out, workspace)
     shp = _shape(q, omega, feature)
     out = torch.empty_like(q) if out is None else out

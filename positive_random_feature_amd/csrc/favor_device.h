@@ -210,8 +210,11 @@ __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_e
 // (softmax-kernel) features, whose exponent x is already in log2 units and
 // shifted; max(x, 0) for the generalised ReLU features (x = log2(e) omega.x,
 // a constant factor that cancels in normalised attention).
+// ReLU features take the IEEE 754-2019 maximum (v_maximum3_f32 on gfx950):
+// unlike fmax it keeps a NaN projection NaN, as max(NaN, 0) in the exact
+// formula, and still maps the -inf of masked rows to 0.
 template <bool RELU> __device__ __forceinline__ float feat(float x) {
-    if constexpr (RELU) return __builtin_fmaxf(x, 0.0f);
+    if constexpr (RELU) return __builtin_elementwise_maximum(x, 0.0f);
     else return exp2f_fast(x);
 }
 

@@ -2254,7 +2254,7 @@ __global__ __launch_bounds__(256) void features_kernel(const T* __restrict__ x, 
         for (int ks = 0; ks < KSD; ++ks) p = mma32(omh[((size_t)ft * KSD + ks) * 64 + lane], xv[ks], p);
         f4 e;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = RELU ? rscale * __builtin_fmaxf(p[i], 0.0f) : exp2f_fast(p[i]);
+        for (int i = 0; i < 4; ++i) e[i] = RELU ? rscale * feat<true>(p[i]) : exp2f_fast(p[i]);
         if (ok) store4(phi + (size_t)row * m + 16 * ft + 4 * g, e);
     }
 }

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kWavesHf * 64) void hadamard_features_kernel(const 
             f4 e;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                e[i] = RELU ? rscale * __builtin_fmaxf(v[j + i], 0.0f) : exp2f_fast(__builtin_fmaf(kLog2e, v[j + i], off));
+                e[i] = RELU ? rscale * feat<true>(v[j + i]) : exp2f_fast(__builtin_fmaf(kLog2e, v[j + i], off));
             *reinterpret_cast<f4*>(tr + j) = e;
         }
         __syncthreads();

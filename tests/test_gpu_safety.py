@@ -5,8 +5,9 @@
   ragged length the padding is unchanged (nothing written out of bounds),
   the inputs are unchanged (nothing written into them), and the result still
   matches the oracle.
-- NaN propagation: a NaN in one row of the inputs gives NaN exactly where the
-  exact formula (the fp64 oracle on the same inputs) gives it: a NaN key
+- NaN propagation, with positive and with ReLU features: a NaN in one row of
+  the inputs gives NaN exactly where the exact formula (the fp64 oracle on
+  the same inputs) gives it: a NaN key
   poisons every output of its head that attends to it (bidirectional: all
   rows; causal: rows at or after it), a NaN query only its own row, a NaN in
   one value element that column of the rows that attend to it.  One
@@ -157,6 +158,54 @@ def test_nan_propagation(d, m, op, where, t):
     assert _rel(got[ok], want[ok]) <= 2e-2
 
 
+@pytest.mark.parametrize("d,m", [(64, 256), (128, 512), (32, 64)])
+@pytest.mark.parametrize("op", ["bidir", "causal"])
+@pytest.mark.parametrize("where,t", [("k", 700), ("q", 455), ("v", 1234)])
+def test_nan_propagation_relu(d, m, op, where, t):
+    """ReLU features keep a NaN too: max(NaN, 0) is NaN in the exact formula
+    (the numpy oracle's maximum), so a NaN key row spreads as with positive
+    features instead of dropping out as a zero feature vector."""
+    B, H, L = 1, 3, 2000
+    vals, dev, om = _nan_case(d, m, B, H, L, where, t, col=d // 2 + 3)
+    fn = favor.bidir if op == "bidir" else favor.causal
+    got = fn(*dev, torch.from_numpy(om).to(DEV), feature="relu").float().cpu().numpy().astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        want = (ref.bidir if op == "bidir" else ref.causal)(*vals, om, kind="relu")
+    nan_want, nan_got = np.isnan(want), np.isnan(got)
+    if op == "causal" and where == "v":
+        chunk = 64 if (d, m) == (64, 256) else 32
+        c0 = (t // chunk) * chunk
+        nan_want = nan_want.copy()
+        nan_want[0, 1, c0:t, d // 2 + 3] = True
+    print(f"[safety] NaN in {where}[{t}] {op} relu d={d} m={m}: {int(nan_want.sum())} NaN expected, "
+          f"{int(nan_got.sum())} produced", flush=True)
+    assert nan_want.any()
+    np.testing.assert_array_equal(nan_got, nan_want)
+    ok = ~nan_want
+    assert np.isfinite(got[ok]).all()
+    assert _rel(got[ok], want[ok]) <= 2e-2
+
+
+@pytest.mark.parametrize("d,m", [(32, 32), (64, 256)])
+@pytest.mark.parametrize("where,t", [("k", 300), ("q", 255), ("v", 411)])
+def test_nan_propagation_relu_one_kernel(d, m, where, t):
+    """ReLU NaN patterns through the one-kernel bidirectional paths."""
+    B, H, L = 1, 3, 500
+    vals, dev, om = _nan_case(d, m, B, H, L, where, t, col=d // 2 + 3)
+    got = favor.bidir(*dev, torch.from_numpy(om).to(DEV), feature="relu", segments=1)
+    got = got.float().cpu().numpy().astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        want = ref.bidir(*vals, om, kind="relu")
+    nan_want, nan_got = np.isnan(want), np.isnan(got)
+    print(f"[safety] NaN in {where}[{t}] one-kernel bidir relu d={d} m={m}: {int(nan_want.sum())} NaN expected, "
+          f"{int(nan_got.sum())} produced", flush=True)
+    assert nan_want.any()
+    np.testing.assert_array_equal(nan_got, nan_want)
+    ok = ~nan_want
+    assert np.isfinite(got[ok]).all()
+    assert _rel(got[ok], want[ok]) <= 2e-2
+
+
 @pytest.mark.parametrize("d,m", [(32, 32), (64, 256)])
 @pytest.mark.parametrize("where,t", [("k", 300), ("k", 0), ("q", 255), ("v", 411), ("k", 499)])
 def test_nan_propagation_one_kernel(d, m, where, t):
@@ -177,3 +226,31 @@ def test_nan_propagation_one_kernel(d, m, where, t):
     ok = ~nan_want
     assert np.isfinite(got[ok]).all()
     assert _rel(got[ok], want[ok]) <= 2e-2
+
+
+@pytest.mark.parametrize("feature", ["positive", "relu"])
+@pytest.mark.parametrize("api", ["dense", "hadamard"])
+@pytest.mark.parametrize("stabilize", [False, True])
+def test_nan_propagation_features(feature, api, stabilize):
+    """One NaN element of x makes that row's features NaN (every projection
+    of the row involves it) and leaves every other row finite, as in the
+    exact formula."""
+    B, H, L, d, m = 1, 2, 100, 64, 256
+    w = WORKLOADS["causal_bf16_8k"].replace(d=d, m=m)
+    inp = make_inputs(w, B=B, H=H, L=L, seed=5)
+    bits = inp.q_bits.copy()
+    bits[0, 1, 37, 11] = 0x7FC0
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    if api == "dense":
+        om = torch.from_numpy(ref.orf_omega(2, H, m, d)).to(DEV)
+        phi, _ = favor.features(x, om, stabilize=stabilize, feature=feature)
+    else:
+        phi, _ = favor.features_hadamard(x, 2, m, stabilize=stabilize, feature=feature)
+    phi = phi.cpu().numpy()
+    nan = np.isnan(phi)
+    print(f"[safety] NaN in x features {feature} {api} stabilize={stabilize}: {int(nan.sum())} NaN "
+          f"(expected {m})", flush=True)
+    want = np.zeros_like(nan)
+    want[0, 1, 37, :] = True
+    np.testing.assert_array_equal(nan, want)
+    assert np.isfinite(phi[~want]).all()
