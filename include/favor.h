@@ -38,7 +38,8 @@
  *     bidirectional and features: m a multiple of 32 up to 256, or a
  *     multiple of 64 up to 512; causal: m in {32, 64, 128, 256, 512}, except
  *     fp32 with d = 64 and m = 512 (its scan's tiles exceed the LDS);
- *     B, H >= 1; L >= 0 (L = 0 is a no-op); B*H*L*d < 2^31.
+ *     B, H >= 1; B*H <= 65535 (one grid row per batch and head); L >= 0
+ *     (L = 0 is a no-op); B*H*L*d < 2^31.
  */
 #ifndef FAVOR_H_
 #define FAVOR_H_
@@ -115,7 +116,7 @@ favor_status favor_features(const favor_shape *shape, const void *x, const float
  * the features in O(L m log d)).  The signs are drawn from the seed inside
  * the call; no workspace, and the projection is exact in fp32 (no rounding
  * of omega to the input dtype).  Same shapes, outputs, stabiliser and
- * overlap rules as favor_features (x, phi, log_scale); B * H <= 65535.
+ * overlap rules as favor_features (x, phi, log_scale).
  */
 favor_status favor_features_hadamard(const favor_shape *shape, const void *x, unsigned long long seed, float *phi,
                                      float *log_scale, int stabilize, void *stream);

@@ -41,6 +41,9 @@ favor_status check_shape(const favor_shape* s, int op) {
         elems *= f;
         if (elems >= (1LL << 31)) return FAVOR_ERR_UNSUPPORTED;
     }
+    // the kernels index (batch, head) pairs with a grid dimension whose
+    // hardware limit is 65535
+    if ((long long)s->B * s->H > 65535) return FAVOR_ERR_UNSUPPORTED;
     if (op == FAVOR_OP_CAUSAL && favor::causal_smem_bytes(dtype_bytes(s->dtype), s->d, s->m) > favor::kMaxLds)
         return FAVOR_ERR_UNSUPPORTED;
     return FAVOR_OK;
@@ -300,7 +303,6 @@ favor_status favor_features_hadamard(const favor_shape* shape, const void* x, un
     const favor_shape* s = shape;
     favor_status st = check_shape(s, FAVOR_OP_FEATURES);
     if (st != FAVOR_OK) return st;
-    if (s->B * s->H > 65535) return FAVOR_ERR_UNSUPPORTED;  // one grid row per (batch, head)
     if (s->L == 0) return FAVOR_OK;
     const size_t xbytes = (size_t)s->B * s->H * s->L * s->d * dtype_bytes(s->dtype);
     const size_t pbytes = (size_t)s->B * s->H * s->L * s->m * sizeof(float);

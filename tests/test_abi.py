@@ -96,6 +96,12 @@ def test_validation(lib, fn):
     assert fn(lib, shp(), nbytes=need - 1) == WORKSPACE
     assert fn(lib, shp(L=0), q=None, k=None, v=None, o=None, ws=None, nbytes=0) == OK  # L = 0: no-op
     assert fn(lib, shp(B=1 << 16, H=1 << 8, L=1 << 8, d=64)) == UNSUPPORTED            # > 2^31 elements
+    # more than 65535 (batch, head) pairs: unsupported even where the element
+    # count fits, rejected before any pointer is looked at
+    assert fn(lib, shp(B=65536, H=1, L=1, d=16), q=None, o=None, ws=None) == UNSUPPORTED
+    assert fn(lib, shp(B=257, H=256, L=4, d=16), q=None, o=None, ws=None) == UNSUPPORTED
+    assert lib.favor_workspace_bytes(1 if fn is _bidir else 2, ctypes.byref(shp(B=65536, H=1, L=1, d=16)), 0) == 0
+    assert lib.favor_workspace_bytes(1 if fn is _bidir else 2, ctypes.byref(shp(B=65535, H=1, L=1, d=16)), 0) > 0
 
 
 def documented_support(dtype, d, m, op):
