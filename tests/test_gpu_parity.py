@@ -8,6 +8,9 @@ run at their full sizes (the longest causal one on sampled rows the oracle
 computes one by one).
 """
 
+import os
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +19,9 @@ import oracle.native as native
 import oracle.reference as ref
 import positive_random_feature_amd as favor
 from positive_random_feature_amd.workloads import WORKLOADS, make_inputs
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from bf16_rounding import features_bf16_operand, fp32_feature_bound  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -330,6 +336,32 @@ def test_features_parity(name):
     assert _rel(phs * np.exp(ls)[..., None], want) <= TOL[w.dtype]
     s_want = np.stack([ref.features_stabilized(inp.q[0, h], oms[h])[1] for h in range(H)])[None]
     assert np.abs(ls - s_want).max() <= (1e-4 if w.dtype == "f32" else 0.05 * (1 + np.abs(s_want).max()))
+
+
+@pytest.mark.parametrize("name", ["bidir_bf16_4k", "causal_bf16_64k"])
+def test_features_bf16_operand_exact(name):
+    """bf16 features differ from the definition by one rounding alone: the
+    projection operand log2(e) * omega in bf16, which the matrix cores need.
+    Against the definition evaluated with that operand, every head is within
+    the a-priori error bound of fp32 arithmetic on its exponents (plain and
+    stabilised), 30 to 150 times tighter than the bf16 bar against the exact
+    definition."""
+    w = WORKLOADS[name]
+    H = 2
+    inp = make_inputs(w, B=1, H=H, L=333)
+    om = _omega(w, H)
+    oms = om if om.ndim == 3 else np.stack([om] * H)
+    x = _to_dev(inp, w.dtype)[0]
+    phi, _ = favor.features(x, torch.from_numpy(om).to(_dev()))
+    phs, ls = favor.features(x, torch.from_numpy(om).to(_dev()), stabilize=True)
+    got = phi.cpu().numpy().astype(np.float64)[0]
+    got_s = (phs.cpu().numpy().astype(np.float64) * np.exp(ls.cpu().numpy().astype(np.float64))[..., None])[0]
+    for h in range(H):
+        emu = features_bf16_operand(inp.q[0, h], oms[h])
+        bound = fp32_feature_bound(inp.q[0, h], oms[h])
+        e1, e2 = _rel(got[h], emu), _rel(got_s[h], emu)
+        _log(f"features {name} head {h} against the bf16-operand definition", max(e1, e2), bound)
+        assert e1 <= bound and e2 <= bound
 
 
 @pytest.mark.parametrize("name", ["bidir_f32_tiny", "bidir_bf16_4k"])
