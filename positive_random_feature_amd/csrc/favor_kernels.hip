@@ -46,9 +46,22 @@
 
 namespace favor {
 
+// d = 16 in bf16: the 32-deep contraction of a bf16 matrix instruction has
+// 16 slots of padding.  Instead of zeros they carry the input row again
+// (x operand) against the low part of log2(e) omega, bf16(v - bf16(v)) for
+// v = log2(e) omega in fp32 (projection operand), so that one instruction
+// computes x . (hi + lo): the projection then carries log2(e) omega to
+// about 2^-17 instead of bf16's 2^-9, at no extra matrix work.  The rounding
+// of that operand is otherwise the largest error term of the bf16 path, and
+// at d = 16 it reaches the 2e-2 bar on some heads.  Row norms never include
+// the repeated half.  fp32 keeps zero padding (its low part is 0).
+template <typename T, int D>
+inline constexpr bool kSplitD16 = sizeof(T) == 2 && D == 16;
+
 // ---------------------------------------------------------------------------
 // omega packing: A-operand order for the projection D[F x T] = Omega'[F x d] X^T.
-// Entry ((ft * KSD + ks) * 64 + lane) holds Omega'[16 ft + r][32 ks + 8 g + j].
+// Entry ((ft * KSD + ks) * 64 + lane) holds Omega'[16 ft + r][32 ks + 8 g + j]
+// (d = 16 in bf16: the low part of Omega'[16 ft + r][8 g - 16 + j] for g >= 2).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pack_omega_kernel(const float* __restrict__ omega, vec8<T>* __restrict__ out,
@@ -70,8 +83,14 @@ __global__ __launch_bounds__(256) void pack_omega_kernel(const float* __restrict
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int c = 32 * ks + 8 * g + j;
-            const float x = c < D ? omega[((size_t)h * m + f) * D + c] * kLog2e : 0.0f;
-            v[j] = (T)x;
+            if (c < D) {
+                v[j] = (T)(omega[((size_t)h * m + f) * D + c] * kLog2e);
+            } else if (kSplitD16<T, D>) {  // the low part (see kSplitD16)
+                const float x = omega[((size_t)h * m + f) * D + c - D] * kLog2e;
+                v[j] = (T)(x - (float)(T)x);
+            } else {
+                v[j] = (T)0.0f;
+            }
         }
         out[idx] = v;
     }
@@ -210,7 +229,10 @@ struct Prefetch {
 template <typename T, int D>
 __device__ __forceinline__ vec8<T> row_operand(const T* tile, int row, int ks, int g) {
     constexpr int RS = LdsTile<T, D>::RS;
-    if (D < 32 && g >= D / 8) return zero8<T>();
+    if (D < 32 && g >= D / 8) {
+        if constexpr (kSplitD16<T, D>) return *reinterpret_cast<const vec8<T>*>(tile + row * RS + 8 * (g - 2));
+        return zero8<T>();
+    }
     return *reinterpret_cast<const vec8<T>*>(tile + row * RS + 32 * ks + 8 * g);
 }
 
@@ -220,11 +242,15 @@ template <typename T, int D>
 __device__ __forceinline__ vec8<T> omega_operand(const float* om_head, int f, int ks, int g) {
     vec8<T> v;
     const int c0 = 32 * ks + 8 * g;
-    if (c0 >= D) return zero8<T>();
-    const float4 a = *reinterpret_cast<const float4*>(om_head + (size_t)f * D + c0);
-    const float4 b = *reinterpret_cast<const float4*>(om_head + (size_t)f * D + c0 + 4);
-    v[0] = (T)(a.x * kLog2e); v[1] = (T)(a.y * kLog2e); v[2] = (T)(a.z * kLog2e); v[3] = (T)(a.w * kLog2e);
-    v[4] = (T)(b.x * kLog2e); v[5] = (T)(b.y * kLog2e); v[6] = (T)(b.z * kLog2e); v[7] = (T)(b.w * kLog2e);
+    if (c0 >= D && !kSplitD16<T, D>) return zero8<T>();
+    const bool lo = c0 >= D;  // the low part (see kSplitD16)
+    const int c = lo ? c0 - D : c0;
+    const float4 a = *reinterpret_cast<const float4*>(om_head + (size_t)f * D + c);
+    const float4 b = *reinterpret_cast<const float4*>(om_head + (size_t)f * D + c + 4);
+    const float x[8] = {a.x * kLog2e, a.y * kLog2e, a.z * kLog2e, a.w * kLog2e,
+                        b.x * kLog2e, b.y * kLog2e, b.z * kLog2e, b.w * kLog2e};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = lo ? (T)(x[j] - (float)(T)x[j]) : (T)x[j];
     return v;
 }
 
@@ -669,7 +695,9 @@ __device__ __forceinline__ void load_queries(const T* __restrict__ q, size_t xba
         for (int ks = 0; ks < KSD; ++ks) {
             if (D >= 32)
                 xq[tt][ks] = load8(q + xbase + (size_t)t * D + 32 * ks + 8 * g);
-            else  // d = 16: lanes g >= 2 hold the zero padding of the contraction
+            else if (kSplitD16<T, D>)  // d = 16, bf16: lanes g >= 2 repeat the row
+                xq[tt][ks] = load8(q + xbase + (size_t)t * D + 8 * (g & 1));
+            else  // d = 16, fp32: lanes g >= 2 hold the zero padding of the contraction
                 xq[tt][ks] = g < D / 8 ? load8(q + xbase + (size_t)t * D + 8 * g) : zero8<T>();
         }
     }
@@ -681,11 +709,13 @@ template <typename T, int D, bool RELU>
 __device__ __forceinline__ void query_consts(const vec8<T> (&xq)[kOutTiles][D < 32 ? 1 : D / 32],
                                              float (&cq)[kOutTiles]) {
     constexpr int KSD = D < 32 ? 1 : D / 32;
+    const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int tt = 0; tt < kOutTiles; ++tt) {
         float ss = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) ss += sumsq8(xq[tt][ks]);
+        if (D < 32 && g >= D / 8) ss = 0.0f;  // padding lanes: zeros or the repeated row
         cq[tt] = RELU ? 0.0f : -0.5f * kLog2e * col_sum(ss);
     }
 }
@@ -2219,12 +2249,15 @@ __global__ __launch_bounds__(256) void features_kernel(const T* __restrict__ x, 
     float ss = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) {
-        const bool in = ok && (D >= 32 || g < D / 8);
-        xv[ks] = in ? load8(x + (size_t)row * D + 32 * ks + 8 * g) : zero8<T>();
+        const bool pad = D < 32 && g >= D / 8;  // padding lanes of d = 16
+        if (kSplitD16<T, D>)  // repeat the row there (see kSplitD16)
+            xv[ks] = ok ? load8(x + (size_t)row * D + 8 * (g & 1)) : zero8<T>();
+        else
+            xv[ks] = ok && !pad ? load8(x + (size_t)row * D + 32 * ks + 8 * g) : zero8<T>();
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float t = to_f(xv[ks][j]);
-            ss += t * t;
+            ss += pad ? 0.0f : t * t;
         }
     }
     const float c = -0.5f * kLog2e * col_sum(ss);

@@ -10,7 +10,7 @@ import numpy as np
 import torch
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from bf16_rounding import LOG2E, features_bf16_operand, round_bf16  # noqa: E402
+from bf16_rounding import LOG2E, features_bf16_operand, projection_operand, round_bf16  # noqa: E402
 
 import oracle.reference as ref  # noqa: E402
 
@@ -39,3 +39,15 @@ def test_features_helper_is_the_definition_for_bf16_operands():
     got = features_bf16_operand(x, om_exact)
     want = ref.features(x, om_exact)
     assert np.max(np.abs(got - want) / want) < 1e-12
+
+
+def test_projection_operand_split_at_d16():
+    """At d = 16 the operand is hi + lo: within 2^-16 of log2(e) omega in
+    fp32 (bf16 alone: 2^-8), and exactly hi elsewhere."""
+    om16 = ref.orf_omega(5, 1, 64, 16)[0]
+    v = (om16 * LOG2E).astype(np.float32).astype(np.float64)
+    op = projection_operand(om16)
+    assert np.max(np.abs(op - v) / np.abs(v)) <= 2.0 ** -16
+    assert np.max(np.abs(round_bf16(v) - v) / np.abs(v)) > 2.0 ** -12  # bf16 alone is far coarser
+    om32 = ref.orf_omega(5, 1, 64, 32)[0]
+    np.testing.assert_array_equal(projection_operand(om32), round_bf16(om32 * LOG2E))
