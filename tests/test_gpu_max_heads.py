@@ -67,9 +67,7 @@ def test_max_heads(op, d, m, L, segments):
 
 
 def test_max_heads_features():
-    # 64 tokens per head: the per-head figure of the raw features follows the
-    # rounding of the bf16 projection operand more closely than attention
-    # outputs do (no ratio cancels it), so each head gets enough elements
+    # 64 tokens per head, so that each head's figure covers enough elements
     d, m, L = 16, 32, 64
     inp, (q, _k, _v), om = _inputs(d, m, L, seed=77)
     print(f"[max-heads] features d={d} m={m} {BH}x1x{L}", flush=True)
@@ -78,10 +76,11 @@ def test_max_heads_features():
     got = phi.cpu().numpy().astype(np.float64)
     want = ref.features(inp.q, om)
     _check(f"features d={d} m={m} L={L}", got, want)
-    # Nearly all of that error is the one rounding the matrix cores need: the
-    # projection operand log2(e) * omega in bf16 (q is bf16 already).  Against
-    # the definition evaluated in fp64 with that operand rounded the same way,
-    # every head is within the a-priori error bound of fp32 arithmetic.
+    # The one rounding the matrix cores need is that of the projection
+    # operand log2(e) * omega (q is bf16 already), carried at d = 16 as a high
+    # and a low bf16 part.  Against the definition evaluated in fp64 with that
+    # operand, every head is within the a-priori error bound of fp32
+    # arithmetic.
     emu = features_bf16_operand(inp.q.reshape(BH, L, d), om)
     diff = (got.reshape(BH, L, m) - emu).reshape(BH, -1)
     per_head = np.linalg.norm(diff, axis=1) / np.linalg.norm(emu.reshape(BH, -1), axis=1)
