@@ -475,6 +475,49 @@ def time_streaming(hip, dev, stream, name="causal_bf16_8k", pieces=8, reps=50):
             "us_per_sequence": ms * 1e3, "tokens_per_s": w.tokens / (ms * 1e-3)}
 
 
+def time_decode(hip, dev, stream, name="causal_bf16_8k", B=64, H=16, steps=32, reps=20):
+    """Decoding: B x H heads of the causal workload's shape, one token per
+    call, each call continuing from the previous call's state
+    (favor_causal_state, the one-launch path for calls of at most 32 tokens
+    per head).  Every step must read and write the heads' fp32 states; their
+    bytes per step over the step time is the reported rate."""
+    w = WORKLOADS[name].replace(B=B, H=H, L=steps)
+    inp = make_inputs(w)
+    lib = _lib.load()
+    toks = [torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
+    om = favor.orf_omega(w.seed, H if w.omega_per_head else 1, w.m, w.d)
+    omega = (om if w.omega_per_head else om[0]).contiguous().to(dev)
+    q1 = toks[0][:, :, :1].contiguous()
+    shape = favor._shape(q1, omega)
+    ws = torch.empty(favor.workspace_bytes(_lib.FAVOR_OP_CAUSAL, shape), dtype=torch.uint8, device=dev)
+    n = favor.state_floats(w.m, w.d)
+    states = [torch.zeros((B, H, n), dtype=torch.float32, device=dev) for _ in range(2)]
+    pieces = [tuple(t[:, :, i:i + 1].contiguous() for t in toks) for i in range(steps)]
+    out = torch.empty_like(q1)
+
+    def run_all():
+        for i, (q, k, v) in enumerate(pieces):
+            sin = states[(i + 1) % 2].data_ptr() if i > 0 else None
+            st = lib.favor_causal_state(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        omega.data_ptr(), out.data_ptr(), 0, sin, states[i % 2].data_ptr(),
+                                        ws.data_ptr(), ws.numel(), stream)
+            _lib.check(st, "favor_causal_state")
+
+    for _ in range(2):
+        run_all()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(reps):
+        run_all()
+    hip.record(e1, stream)
+    us = hip.elapsed_ms(e0, e1) / (reps * steps) * 1e3
+    state_bytes = 2 * B * H * n * 4
+    return {"heads": B * H, "d": w.d, "m": w.m, "tokens_per_call_per_head": 1, "us_per_step": us,
+            "tokens_per_s": B * H / (us * 1e-6), "state_mb_per_step": state_bytes / 1e6,
+            "state_gbs": state_bytes / (us * 1e-6) / 1e9}
+
+
 # ---------------------------------------------------------------------------
 # Profiler summaries (rocprofv3 CSV output of runs of this script)
 # ---------------------------------------------------------------------------
@@ -882,6 +925,7 @@ def main():
     if not args.no_configs:
         result["configs"] = time_configs(hip, dev, stream)
         result["streaming"] = time_streaming(hip, dev, stream)
+        result["decode"] = time_decode(hip, dev, stream)
         result["hadamard_projection"] = time_hadamard(hip, dev, stream)
         result["givens_projection"] = time_givens(hip, dev, stream)
         result["structured_features"] = time_structured_features(hip, dev, stream)

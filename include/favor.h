@@ -205,7 +205,11 @@ favor_status favor_causal_plan(const favor_shape *shape, const void *q, const vo
  * state_in: NULL = no keys seen yet.  A state with S = z = 0 should be passed
  * as NULL: its shift still takes part in the key stabiliser.
  * state_out: NULL = not written; otherwise it receives the state including
- * this call's keys, with one shift per head.  state_out must not overlap
+ * this call's keys, with one shift per head.
+ * Calls of at most 32 tokens per head (decoding) run as one kernel that
+ * reads state_in and writes state_out itself, for every shape with a
+ * feature-split scan (all but bf16 with d = 128 and m >= 256); the
+ * workspace is still required and validated.  state_out must not overlap
  * state_in, q, k, v, out, omega or ws, and state_in must not overlap out or
  * ws (FAVOR_ERR_INVALID_ARG).  Both must be
  * 4-byte aligned.  L = 0 writes nothing.  Positive features only

@@ -74,6 +74,10 @@ hipError_t launch_hadamard_features(const HadamardFeaturesArgs& a);
 // Tokens per step of the causal chunked scan for a shape.
 int causal_chunk_tokens(int dtype_bytes, int D, int m);
 CausalCfg causal_config(int dtype_bytes, int D, int m);
+// Shapes with a one-launch path for causal calls that carry a state over at
+// most one 32-token chunk per head.
+bool causal_decode_shape(int dtype_bytes, int D, int m);
+constexpr int kDecodeMaxTokens = 32;
 // Shapes whose causal scan is the d = 128 column-half scan (causal_wide).
 bool causal_wide_shape(int dtype_bytes, int D, int m);
 // LDS bytes the causal kernel needs (SIZE_MAX when the shape is unsupported).

@@ -1484,6 +1484,233 @@ __global__ __launch_bounds__(64 * W) void causal_chunk_kernel(const T* __restric
 }
 
 // ---------------------------------------------------------------------------
+// causal_decode: a causal call that carries a state and holds at most one
+// 32-token chunk per head (decoding, short streaming pieces), in one launch
+// instead of the segment-sum, merge/scan and scan launches and their
+// workspace round trips.  One workgroup of W waves per (batch, head); wave w
+// owns features [FW w, FW w + FW) as in causal_chunk, whose chunk arithmetic
+// it repeats:
+//   1. the chunk's keys are projected first; the key shift M is the larger
+//      of the incoming state's shift and the largest key exponent (over the
+//      waves, through LDS), so every feature and the rescaled state are <= 1;
+//   2. the state is read from state_in (per head: G[m][D] row-major, z[m],
+//      natural-log shift s; true values = stored e^s) straight into the
+//      registers of the segment-sum layout, rescaled to M (zero without one);
+//   3. the projection operands come from the fp32 projection (no packed copy
+//      is needed by an earlier pass);
+//   4. outputs as in causal_chunk; the new state goes to state_out from the
+//      registers, with the shift M (ln 2 M in natural-log units).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int FW, int W>
+__global__ __launch_bounds__(64 * W) void causal_decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                               const T* __restrict__ v, const float* __restrict__ omega,
+                                                               int om_per_head, const float* __restrict__ state_in,
+                                                               float* __restrict__ state_out, T* __restrict__ out, int H,
+                                                               int L, int m) {
+    using TL = LdsTile<T, D>;
+    using PTL = LdsTile<T, FW>;
+    using SM = CausalSmem<T, D, FW, W, 1>;
+    constexpr int RS = TL::RS;
+    constexpr int KSD = D < 32 ? 1 : D / 32;
+    constexpr int NT = D / 16 + 1;
+    constexpr int NFT = FW / 16;
+    constexpr int KSF = FW / 32;
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    __shared__ float wave_max[W];
+    T* kt = reinterpret_cast<T*>(smem_raw);
+    T* qt = kt + TL::ELEMS;
+    T* vt = qt + TL::ELEMS;
+    float* part = reinterpret_cast<float*>(smem_raw + SM::OFF_PART);
+    float* plam = reinterpret_cast<float*>(smem_raw + SM::OFF_LAM);
+    float* nrm = reinterpret_cast<float*>(smem_raw + SM::OFF_NRM);  // [K rows, Q rows]
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
+    const int bh = blockIdx.x, h = bh % H;
+    const int f0 = w * FW;
+    const size_t xbase = (size_t)bh * L * D;
+    const size_t st_stride = (size_t)m * (D + 1) + 1;
+    const float* omh = omega + (om_per_head ? (size_t)h * m * D : 0);
+    T* ptw = reinterpret_cast<T*>(smem_raw + SM::OFF_PT) + (size_t)w * PTL::ELEMS;
+
+    // the chunk (rows past L zeroed), the carried state (raw; scaled once the
+    // shift is known) and this wave's projection operands, all requested
+    // before the first barrier.  The state sits in the registers of the
+    // segment-sum layout: G[ft][nt][i] holds G[f0 + 16 ft + 4 g + i][16 nt + r]
+    // (nt < NT - 1) or z
+    const Ptrs<const T*> src{k + xbase, q + xbase, v + xbase};
+    Prefetch<T, D, 64 * W, 3> pf;
+    pf.load(src, 0, L - 1);
+    auto st_index = [&](int ft, int nt, int i) -> size_t {
+        const int f = f0 + 16 * ft + 4 * g + i;
+        return nt < NT - 1 ? (size_t)f * D + 16 * nt + r : (size_t)m * D + f;
+    };
+    const float* si = state_in ? state_in + (size_t)bh * st_stride : nullptr;
+    f4 G[NFT][NT];
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G[ft][nt][i] = si ? si[st_index(ft, nt, i)] : 0.0f;
+    const float Ms = si ? si[(size_t)m * (D + 1)] * kLog2e : kNegInf;
+    vec8<T> om[NFT][KSD];
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) om[ft][ks] = omega_operand<T, D>(omh, f0 + 16 * ft + r, ks, g);
+    pf.store(Ptrs<T*>{kt, qt, vt}, nrm, 3, 0, L);
+    __syncthreads();
+
+    // ---- key projections (log2 units, relative to 0) and the key shift
+    f4 pk[2][NFT];
+    float lm = kNegInf;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        vec8<T> x[KSD];
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) x[ks] = row_operand<T, D>(kt, 16 * tt + r, ks, g);
+        const float c = 16 * tt + r < L ? nrm[16 * tt + r] : kNegInf;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+            pk[tt][ft] = f4splat(c);
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) pk[tt][ft] = mma32(om[ft][ks], x[ks], pk[tt][ft]);  // D[F x T]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lm = __builtin_fmaxf(lm, pk[tt][ft][i]);
+        }
+    }
+    lm = wave_max_uniform(lm);
+    if (lane == 0) wave_max[w] = lm;
+    __syncthreads();
+    float M = Ms;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) M = __builtin_fmaxf(M, wave_max[ww]);
+
+    // ---- the carried state rescaled to M
+    const float sc = si ? exp2f_fast(Ms - M) : 0.0f;
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) G[ft][nt] *= sc;
+
+    // ---- key features relative to M: the A operand of the intra-chunk
+    // scores and, row-major by token in LDS, of the state update
+    vec8<T> ak[2][KSF];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pk[tt][ft][i] = exp2f_fast(pk[tt][ft][i] - M);
+            lds_store4(ptw + (16 * tt + r) * PTL::RS + 16 * ft + 4 * g, pk[tt][ft]);
+        }
+#pragma unroll
+        for (int kf = 0; kf < KSF; ++kf) ak[tt][kf] = pack8t<T>(pk[tt][2 * kf], pk[tt][2 * kf + 1]);
+    }
+
+    // ---- queries: projection and a per-token shift over this wave's features
+    vec8<T> bq[2][KSF];
+    float sq[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        vec8<T> x[KSD];
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) x[ks] = row_operand<T, D>(qt, 16 * tt + r, ks, g);
+        const float c = nrm[32 + 16 * tt + r];
+        f4 pq[NFT];
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) {
+            pq[ft] = f4splat(c);
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) pq[ft] = mma32(om[ft][ks], x[ks], pq[ft]);
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, pq[ft][i]);
+        mx = col_max(mx);
+        sq[tt] = mx;
+#pragma unroll
+        for (int kf = 0; kf < KSF; ++kf) {
+            f4 e0, e1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e0[i] = exp2f_fast(pq[2 * kf][i] - mx);
+                e1[i] = exp2f_fast(pq[2 * kf + 1][i] - mx);
+            }
+            bq[tt][kf] = pack8t<T>(e0, e1);
+        }
+    }
+
+    // ---- intra-chunk S^T[T_k x T_q], masked T_k <= T_q
+    f4 S[2][2];
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) {
+            S[tk][tq] = f4splat(0.0f);
+            if (tk <= tq) {
+#pragma unroll
+                for (int kf = 0; kf < KSF; ++kf) S[tk][tq] = mma32(ak[tk][kf], bq[tq][kf], S[tk][tq]);
+            }
+        }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * g + i > r) S[t][t][i] = 0.0f;
+    vec8<T> bs[2];
+#pragma unroll
+    for (int tq = 0; tq < 2; ++tq) bs[tq] = pack8t<T>(S[0][tq], S[1][tq]);
+
+    // ---- partial outputs over this wave's features, and G += phi(K)^T [V | 1]
+    float* pw = part + (size_t)w * 32 * SM::PART_STRIDE;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        vec8<T> ga[KSF];
+#pragma unroll
+        for (int kf = 0; kf < KSF; ++kf) ga[kf] = pack8t<T>(G[2 * kf][nt], G[2 * kf + 1][nt]);
+        const vec8<T> va = nt < NT - 1 ? kappa_col<RS>(vt, 16 * nt, lane) : splat8<T>(1.0f);
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) {
+            f4 o = f4splat(0.0f);
+#pragma unroll
+            for (int kf = 0; kf < KSF; ++kf) o = mma32(ga[kf], bq[tq][kf], o);
+            o = mma32(va, bs[tq], o);
+            float* row = pw + (16 * tq + r) * SM::PART_STRIDE;
+            if (nt < NT - 1) {
+                *reinterpret_cast<float4*>(row + 16 * nt + 4 * g) = float4{o[0], o[1], o[2], o[3]};
+            } else if (g == 0) {
+                row[D] = o[0];
+            }
+        }
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) G[ft][nt] = mma32(kappa_col<PTL::RS>(ptw, 16 * ft, lane), va, G[ft][nt]);
+    }
+    if (g == 0) {
+        plam[w * 32 + r] = sq[0] + M;
+        plam[w * 32 + 16 + r] = sq[1] + M;
+    }
+    __syncthreads();
+    causal_reduce<T, D, FW, W, 1>(part, plam, out, xbase, 0, L);
+
+    // ---- the new state, relative to M (z: every column of its tile holds it)
+    if (state_out) {
+        float* so = state_out + (size_t)bh * st_stride;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                if (nt < NT - 1 || r == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) so[st_index(ft, nt, i)] = G[ft][nt][i];
+                }
+        if (threadIdx.x == 0) so[(size_t)m * (D + 1)] = M * 0.69314718055994531f;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // causal_tile: chunked causal scan for bf16, d = 64, m <= 256.  One workgroup
 // of eight waves per (segment, head); chunks of 64 tokens.  Waves s and s + 4
 // (which share a SIMD) own token tile s (tokens 16s..16s+15 of the chunk) and
@@ -2344,6 +2571,42 @@ static hipError_t launch_causal(const LaunchArgs& a, const vec8<T>* ompack, long
     return hipGetLastError();
 }
 
+template <typename T, int D, int FW, int W>
+static hipError_t launch_causal_decode(const LaunchArgs& a, const T* q, const T* k, const T* v, T* out) {
+    constexpr size_t bytes = CausalSmem<T, D, FW, W, 1>::BYTES;
+    if constexpr (bytes + sizeof(float) * W > kMaxLds) {
+        return hipErrorInvalidValue;  // not a decode shape (causal_decode_shape)
+    } else {
+        auto kern = causal_decode_kernel<T, D, FW, W>;
+        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(64 * W), bytes, a.stream, q, k, v, a.omega,
+                           a.omega_per_head ? 1 : 0, a.state_in, a.state_out, out, a.H, a.L, a.m);
+        return hipGetLastError();
+    }
+}
+
+// The configuration of causal_decode for this shape: the feature-split
+// scan's (features per wave, waves), among the pairs instantiated for it.
+template <typename T, int D>
+static hipError_t dispatch_causal_decode(const LaunchArgs& a, const T* q, const T* k, const T* v, T* out) {
+    const CausalCfg cfg = causal_config((int)sizeof(T), D, a.m);
+    constexpr bool narrow = (sizeof(T) == 2 && D == 128) || (sizeof(T) == 4 && D == 64);
+    if (cfg.fw == 32 && cfg.w == 1) return launch_causal_decode<T, D, 32, 1>(a, q, k, v, out);
+    if constexpr (narrow) {
+        if (cfg.fw == 32 && cfg.w == 2) return launch_causal_decode<T, D, 32, 2>(a, q, k, v, out);
+        if (cfg.fw == 32 && cfg.w == 4) return launch_causal_decode<T, D, 32, 4>(a, q, k, v, out);
+        if constexpr (sizeof(T) == 4) {
+            if (cfg.fw == 32 && cfg.w == 8) return launch_causal_decode<T, D, 32, 8>(a, q, k, v, out);
+        }
+    } else {
+        if (cfg.fw == 64 && cfg.w == 1) return launch_causal_decode<T, D, 64, 1>(a, q, k, v, out);
+        if (cfg.fw == 64 && cfg.w == 2) return launch_causal_decode<T, D, 64, 2>(a, q, k, v, out);
+        if (cfg.fw == 64 && cfg.w == 4) return launch_causal_decode<T, D, 64, 4>(a, q, k, v, out);
+        if (cfg.fw == 64 && cfg.w == 8) return launch_causal_decode<T, D, 64, 8>(a, q, k, v, out);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int M, bool RELU>
 static hipError_t launch_causal_tile(const LaunchArgs& a, const bf16x8* ompack, long long om_head_vecs, const bf16* q,
                                      const bf16* k, const bf16* v, bf16* out) {
@@ -2403,6 +2666,15 @@ static hipError_t launch_all(const LaunchArgs& a) {
     const int per_head = a.omega_per_head ? 1 : 0;
     const int nfg = (a.m + 255) / 256;
     stage_event(a, 0);
+    // a carried state over at most one chunk per head: one launch
+    if constexpr (!RELU) {
+        if (a.op == OpKind::Causal && (a.state_in || a.state_out) && a.L <= kDecodeMaxTokens &&
+            causal_decode_shape((int)sizeof(T), D, a.m)) {
+            const hipError_t err = dispatch_causal_decode<T, D>(a, q, k, v, out);
+            for (int i = 1; i <= 3; ++i) stage_event(a, i);
+            return err;
+        }
+    }
     constexpr int PD_KV = D >= 128 ? 1 : 2;
     // one segment per head and 32 features: the key-split one-kernel path
     // (fp32 with d = 64 would not fit its registers)

@@ -41,6 +41,16 @@ size_t causal_smem_bytes(int dtype_bytes, int D, int m) {
            sizeof(float) * (size_t)c.w * 32 * (D + 4) + sizeof(float) * (size_t)c.w * 32 + sizeof(float) * 2 * 2 * 32;
 }
 
+bool causal_decode_shape(int dtype_bytes, int D, int m) {
+    // the one-launch path for calls that carry a state over at most one
+    // 32-token chunk: the feature-split scan's configurations (bf16 with
+    // d = 128 and m >= 256 has none: its scan splits the value columns)
+    const CausalCfg c = causal_config(dtype_bytes, D, m);
+    if (c.w == 0) return false;
+    const bool narrow = (dtype_bytes == 2 && D == 128) || (dtype_bytes == 4 && D == 64);
+    return !narrow || c.w <= 4 || (dtype_bytes == 4 && c.w == 8);
+}
+
 bool bidir_small_shape(int dtype_bytes, int D, int m) {
     // the key-split one-kernel path: every wave sums all 32 features over its
     // own keys (its sums and operands fit the registers for these d)

@@ -141,3 +141,95 @@ def test_state_matches_plain_call():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert math.isfinite(float(st[..., -1].max()))
+
+
+# Every configuration of the one-launch path for calls of at most 32 tokens
+# per head that carry a state (features per wave x waves: 32 x 1, 64 x 1..8,
+# 32 x 2..4 for bf16 d = 128, 32 x 2..8 for fp32 d = 64), d = 16 with its
+# split projection operand, and shapes without that path (bf16, d = 128,
+# m = 256 and 512), which keep the three kernels.
+DECODE_CASES = [("bf16", 16, 32), ("bf16", 16, 512), ("bf16", 32, 64), ("bf16", 64, 64), ("bf16", 64, 128),
+                ("bf16", 64, 256), ("bf16", 64, 512), ("bf16", 128, 64), ("bf16", 128, 128), ("bf16", 128, 256),
+                ("bf16", 128, 512), ("f32", 16, 128), ("f32", 32, 512), ("f32", 64, 64), ("f32", 64, 128),
+                ("f32", 64, 256)]
+
+
+@pytest.mark.parametrize("dtype,d,m", DECODE_CASES)
+def test_decode_steps(dtype, d, m):
+    """A prefix in one call, then decode steps of 1 token (and a few of 2 to
+    32) per call, each continuing from the previous state, for 32 heads: the
+    outputs match the oracle's single pass and the final state its prefix
+    sums."""
+    base = WORKLOADS["causal_bf16_8k" if dtype == "bf16" else "bidir_f32_tiny"]
+    w = base.replace(d=d, m=m, omega_per_head=True)
+    B, H = 4, 8
+    steps = [50] + [1] * 12 + [17, 32, 1, 5, 2]
+    L = sum(steps)
+    inp = make_inputs(w, B=B, H=H, L=L, seed=d + m)
+    om = ref.orf_omega(7 + d + m, H, m, d)
+    q, k, v = _to_dev(inp, dtype)
+    om_t = torch.from_numpy(om).to(_dev())
+    outs, st, t = [], None, 0
+    for n in steps:
+        o, st = favor.causal(q[:, :, t:t + n].contiguous(), k[:, :, t:t + n].contiguous(),
+                             v[:, :, t:t + n].contiguous(), om_t, state=st, return_state=True)
+        outs.append(o)
+        t += n
+    torch.cuda.synchronize()
+    got = torch.cat(outs, dim=2).float().cpu().numpy().astype(np.float64)
+    want = native.causal(inp.q, inp.k, inp.v, om)
+    err = _rel(got, want)
+    worst = max(_rel(got[b, h], want[b, h]) for b in range(B) for h in range(H))
+    _log(f"decode steps {dtype} d={d} m={m}: worst head {worst:.3e}, whole", err, TOL[dtype])
+    assert err <= TOL[dtype] and worst <= TOL[dtype]
+    _, (G, z) = ref.causal_with_state(inp.q, inp.k, inp.v, om)
+    Gg, zg = _true_state(st, m, d)
+    eg, ez = _rel(Gg, G), _rel(zg, z)
+    _log(f"decode steps {dtype} d={d} m={m} final state G, z", max(eg, ez), TOL[dtype])
+    assert eg <= TOL[dtype] and ez <= TOL[dtype]
+
+
+def test_decode_large_norms():
+    """Decode steps with entries of q, k at 3 d^-1/4: keys that raise the
+    shift far above the carried one, rescaling the state each step."""
+    w = WORKLOADS["causal_bf16_8k"].replace(qk_scale=3.0, omega_per_head=True)
+    B, H = 2, 8
+    steps = [3] + [1] * 20 + [32]
+    L = sum(steps)
+    inp = make_inputs(w, B=B, H=H, L=L, seed=5)
+    om = ref.orf_omega(w.seed, H, w.m, w.d)
+    q, k, v = _to_dev(inp, "bf16")
+    om_t = torch.from_numpy(om).to(_dev())
+    outs, st, t = [], None, 0
+    for n in steps:
+        o, st = favor.causal(q[:, :, t:t + n].contiguous(), k[:, :, t:t + n].contiguous(),
+                             v[:, :, t:t + n].contiguous(), om_t, state=st, return_state=True)
+        outs.append(o)
+        t += n
+    torch.cuda.synchronize()
+    got = torch.cat(outs, dim=2).float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = _rel(got, native.causal(inp.q, inp.k, inp.v, om))
+    _log("large-norm decode steps", err, 2e-2)
+    assert err <= 2e-2
+    S, z, s = favor.state_parts(st.cpu(), w.m, w.d)
+    assert torch.isfinite(S).all() and torch.isfinite(z).all() and torch.isfinite(s).all()
+
+
+def test_decode_first_and_last_call():
+    """A first call with no state in (state out only) and a last call with no
+    state out, both of a few tokens, against the oracle."""
+    w = WORKLOADS["causal_bf16_8k"].replace(omega_per_head=True)
+    B, H = 3, 4
+    inp = make_inputs(w, B=B, H=H, L=37, seed=9)
+    om = ref.orf_omega(w.seed, H, w.m, w.d)
+    q, k, v = _to_dev(inp, "bf16")
+    om_t = torch.from_numpy(om).to(_dev())
+    a, st = favor.causal(q[:, :, :7].contiguous(), k[:, :, :7].contiguous(), v[:, :, :7].contiguous(), om_t,
+                         return_state=True)
+    b = favor.causal(q[:, :, 7:].contiguous(), k[:, :, 7:].contiguous(), v[:, :, 7:].contiguous(), om_t, state=st)
+    torch.cuda.synchronize()
+    got = torch.cat([a, b], dim=2).float().cpu().numpy().astype(np.float64)
+    err = _rel(got, native.causal(inp.q, inp.k, inp.v, om))
+    _log("decode first and last call", err, 2e-2)
+    assert err <= 2e-2
